@@ -1,0 +1,15 @@
+"""Binary-weight x ternary-activation (BWTA) matrix products for AMD MI355X.
+
+The compute lives in libbwta.so (hand-written HIP kernels for gfx950, C ABI in
+include/bwta.h); this package is its Python binding.  Method: "BWTA: Accurate
+and Efficient Binarized Transformer by Algorithm-Hardware Co-design", Abstract
+(binary weights, ternary activations with tiny values projected to zero,
+bit-packed binary/ternary MatMul for linear and attention operators).
+"""
+from ._binding import (BinaryPlanes, BwtaError, TernaryPlanes, bwta_batched_gemm, bwta_gemm,
+                       bwta_gemv, bwta_pack_weights, bwta_ternarize_pack, lib, padded_k,
+                       row_bytes)
+
+__all__ = ["BinaryPlanes", "BwtaError", "TernaryPlanes", "bwta_batched_gemm", "bwta_gemm",
+           "bwta_gemv", "bwta_pack_weights", "bwta_ternarize_pack", "lib", "padded_k",
+           "row_bytes"]

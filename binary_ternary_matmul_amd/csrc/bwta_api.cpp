@@ -1,0 +1,215 @@
+// bwta_api.cpp - the extern "C" entry points of libbwta.so: argument
+// validation, status codes, kernel selection.  Definitions of the operations
+// are in bwta.h; the kernels are in pack.hip, gemm_mfma.hip, gemm_popcount.hip.
+#include "bwta.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+bwta_status fail(bwta_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bwta_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return BWTA_OK;
+  return fail(BWTA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_io_dtype(bwta_dtype d) { return d == BWTA_F32 || d == BWTA_BF16; }
+bool valid_out_dtype(bwta_dtype d) { return d == BWTA_F32 || d == BWTA_BF16 || d == BWTA_I32; }
+size_t dtype_size(bwta_dtype d) { return d == BWTA_BF16 ? 2 : 4; }
+
+bwta_status check_plane(const void* p, const char* name) {
+  if (!p) return fail(BWTA_ERR_INVALID, "%s is NULL", name);
+  if (!aligned(p, 16)) return fail(BWTA_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return BWTA_OK;
+}
+
+bwta_status check_word(const void* p, bool required, const char* name) {
+  if (!p) return required ? fail(BWTA_ERR_INVALID, "%s is NULL", name) : BWTA_OK;
+  if (!aligned(p, 4)) return fail(BWTA_ERR_ALIGN, "%s is not 4-byte aligned", name);
+  return BWTA_OK;
+}
+
+bwta_status check_k(int64_t K) {
+  if (K <= 0) return fail(BWTA_ERR_INVALID, "K must be positive (got %lld)", (long long)K);
+  if (K > BWTA_MAX_K)
+    return fail(BWTA_ERR_UNSUPPORTED, "K = %lld exceeds BWTA_MAX_K = %d", (long long)K, BWTA_MAX_K);
+  return BWTA_OK;
+}
+
+#define BWTA_TRY(x)                  \
+  do {                               \
+    bwta_status st_ = (x);           \
+    if (st_ != BWTA_OK) return st_;  \
+  } while (0)
+
+bwta_status check_product(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
+                          const int32_t* a_nnz, const uint8_t* b_mask, bool b_ternary,
+                          const uint8_t* b_sign, const float* b_alpha, int64_t M, int64_t N,
+                          int64_t K, const void* Y, bwta_dtype y_dtype, int64_t ldy,
+                          bwta_algo algo) {
+  if (M < 0 || N < 0) return fail(BWTA_ERR_INVALID, "negative size M=%lld N=%lld", (long long)M, (long long)N);
+  BWTA_TRY(check_k(K));
+  if (!valid_out_dtype(y_dtype)) return fail(BWTA_ERR_INVALID, "bad output dtype %d", (int)y_dtype);
+  if (algo != BWTA_ALGO_AUTO && algo != BWTA_ALGO_MFMA && algo != BWTA_ALGO_POPCOUNT)
+    return fail(BWTA_ERR_INVALID, "bad algo %d", (int)algo);
+  if (ldy < N) return fail(BWTA_ERR_INVALID, "ldy (%lld) < N (%lld)", (long long)ldy, (long long)N);
+  if (M == 0 || N == 0) return BWTA_OK;  // empty: pointers may be NULL
+  BWTA_TRY(check_plane(a_mask, "a_mask"));
+  BWTA_TRY(check_plane(a_sign, "a_sign"));
+  if (b_ternary) BWTA_TRY(check_plane(b_mask, "b_mask"));
+  BWTA_TRY(check_plane(b_sign, b_ternary ? "b_sign" : "w_sign"));
+  const bool scaled = y_dtype != BWTA_I32;
+  BWTA_TRY(check_word(a_alpha, scaled, "a_alpha"));
+  BWTA_TRY(check_word(b_alpha, scaled, b_ternary ? "b_alpha" : "w_alpha"));
+  BWTA_TRY(check_word(a_nnz, !b_ternary, "a_nnz"));
+  if (!Y) return fail(BWTA_ERR_INVALID, "Y is NULL");
+  if (!aligned(Y, dtype_size(y_dtype))) return fail(BWTA_ERR_ALIGN, "Y is not aligned to its element");
+  return BWTA_OK;
+}
+
+bwta::Elt elt(bwta_dtype d) {
+  return d == BWTA_F32 ? bwta::Elt::F32 : d == BWTA_BF16 ? bwta::Elt::BF16 : bwta::Elt::I32;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bwta_version(void) { return BWTA_API_VERSION; }
+
+int64_t bwta_padded_k(int64_t K) { return K <= 0 ? 0 : (K + 63) / 64 * 64; }
+int64_t bwta_row_bytes(int64_t K) { return bwta_padded_k(K) / 8; }
+
+const char* bwta_status_string(bwta_status s) {
+  switch (s) {
+    case BWTA_OK: return "BWTA_OK";
+    case BWTA_ERR_INVALID: return "BWTA_ERR_INVALID";
+    case BWTA_ERR_ALIGN: return "BWTA_ERR_ALIGN";
+    case BWTA_ERR_UNSUPPORTED: return "BWTA_ERR_UNSUPPORTED";
+    case BWTA_ERR_HIP: return "BWTA_ERR_HIP";
+  }
+  return "BWTA_ERR_UNKNOWN";
+}
+
+const char* bwta_last_error(void) { return g_last_error; }
+
+bwta_status bwta_pack_weights(const void* W, bwta_dtype w_dtype, int64_t rows, int64_t K,
+                              int64_t stride_row, int64_t stride_k, uint8_t* sign, float* alpha,
+                              void* stream) {
+  if (!valid_io_dtype(w_dtype)) return fail(BWTA_ERR_INVALID, "bad weight dtype %d", (int)w_dtype);
+  if (rows < 0) return fail(BWTA_ERR_INVALID, "negative rows");
+  BWTA_TRY(check_k(K));
+  if (stride_row < 0 || stride_k <= 0) return fail(BWTA_ERR_INVALID, "bad strides");
+  if (rows == 0) return BWTA_OK;  // empty: pointers may be NULL
+  if (!W) return fail(BWTA_ERR_INVALID, "W is NULL");
+  if (!aligned(W, dtype_size(w_dtype))) return fail(BWTA_ERR_ALIGN, "W is not aligned to its element");
+  BWTA_TRY(check_plane(sign, "sign"));
+  BWTA_TRY(check_word(alpha, true, "alpha"));
+  if (rows == 0) return BWTA_OK;
+  return from_hip(bwta::launch_binarize(W, elt(w_dtype), rows, K, stride_row, stride_k, sign, alpha,
+                                        static_cast<hipStream_t>(stream)),
+                  "bwta_pack_weights launch");
+}
+
+bwta_status bwta_ternarize_pack(const void* X, bwta_dtype x_dtype, int64_t rows, int64_t K,
+                                int64_t stride_row, uint8_t* mask, uint8_t* sign, float* alpha,
+                                int32_t* nnz, void* stream) {
+  if (!valid_io_dtype(x_dtype)) return fail(BWTA_ERR_INVALID, "bad activation dtype %d", (int)x_dtype);
+  if (rows < 0) return fail(BWTA_ERR_INVALID, "negative rows");
+  BWTA_TRY(check_k(K));
+  if (stride_row < K && rows > 1) return fail(BWTA_ERR_INVALID, "stride_row < K");
+  if (rows == 0) return BWTA_OK;  // empty: pointers may be NULL
+  if (!X) return fail(BWTA_ERR_INVALID, "X is NULL");
+  if (!aligned(X, dtype_size(x_dtype))) return fail(BWTA_ERR_ALIGN, "X is not aligned to its element");
+  BWTA_TRY(check_plane(mask, "mask"));
+  BWTA_TRY(check_plane(sign, "sign"));
+  BWTA_TRY(check_word(alpha, true, "alpha"));
+  BWTA_TRY(check_word(nnz, true, "nnz"));
+  if (rows == 0) return BWTA_OK;
+  return from_hip(bwta::launch_ternarize(X, elt(x_dtype), rows, K, stride_row, mask, sign, alpha,
+                                         nnz, static_cast<hipStream_t>(stream)),
+                  "bwta_ternarize_pack launch");
+}
+
+static bwta_status run_product(const bwta::GemmArgs& g, bwta_algo algo, bool gemv,
+                               hipStream_t stream) {
+  const int64_t row_bytes = (g.K + 63) / 64 * 8;
+  if (algo == BWTA_ALGO_AUTO) {
+    // Decode rows: the popcount GEMV streams the weights once for M <= 4.
+    algo = (gemv && g.M <= 4 && !g.b_mask) ? BWTA_ALGO_POPCOUNT : BWTA_ALGO_MFMA;
+  }
+  hipError_t e;
+  if (algo == BWTA_ALGO_POPCOUNT) {
+    if (gemv && !g.b_mask && row_bytes % 16 == 0)
+      e = bwta::launch_gemv_popcount(g, stream);
+    else
+      e = bwta::launch_gemm_popcount(g, stream);
+  } else {
+    e = bwta::launch_gemm_mfma(g, stream);
+  }
+  return from_hip(e, "product launch");
+}
+
+bwta_status bwta_gemm(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
+                      const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha, int64_t M,
+                      int64_t N, int64_t K, void* Y, bwta_dtype y_dtype, int64_t ldy,
+                      bwta_algo algo, void* stream) {
+  BWTA_TRY(check_product(a_mask, a_sign, a_alpha, a_nnz, nullptr, false, w_sign, w_alpha, M, N, K,
+                         Y, y_dtype, ldy, algo));
+  if (M == 0 || N == 0) return BWTA_OK;
+  bwta::GemmArgs g{a_mask, a_sign, a_alpha, a_nnz, 0, nullptr, w_sign, w_alpha, 0,
+                   1, M, N, K, Y, elt(y_dtype), ldy, 0};
+  return run_product(g, algo, false, static_cast<hipStream_t>(stream));
+}
+
+bwta_status bwta_gemv(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
+                      const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha, int64_t M,
+                      int64_t N, int64_t K, void* Y, bwta_dtype y_dtype, int64_t ldy,
+                      bwta_algo algo, void* stream) {
+  BWTA_TRY(check_product(a_mask, a_sign, a_alpha, a_nnz, nullptr, false, w_sign, w_alpha, M, N, K,
+                         Y, y_dtype, ldy, algo));
+  if (M > 16) return fail(BWTA_ERR_UNSUPPORTED, "bwta_gemv takes M <= 16 (got %lld)", (long long)M);
+  if (M == 0 || N == 0) return BWTA_OK;
+  bwta::GemmArgs g{a_mask, a_sign, a_alpha, a_nnz, 0, nullptr, w_sign, w_alpha, 0,
+                   1, M, N, K, Y, elt(y_dtype), ldy, 0};
+  return run_product(g, algo, true, static_cast<hipStream_t>(stream));
+}
+
+bwta_status bwta_batched_gemm(int64_t batch, const uint8_t* a_mask, const uint8_t* a_sign,
+                              const float* a_alpha, const int32_t* a_nnz, int64_t a_batch_rows,
+                              const uint8_t* b_mask, const uint8_t* b_sign, const float* b_alpha,
+                              int64_t b_batch_rows, int64_t M, int64_t N, int64_t K, void* Y,
+                              bwta_dtype y_dtype, int64_t ldy, int64_t y_batch_stride,
+                              bwta_algo algo, void* stream) {
+  if (batch < 0) return fail(BWTA_ERR_INVALID, "negative batch");
+  if (a_batch_rows < 0 || b_batch_rows < 0 || y_batch_stride < 0)
+    return fail(BWTA_ERR_INVALID, "negative batch stride");
+  if (batch > 65535) return fail(BWTA_ERR_UNSUPPORTED, "batch > 65535");
+  if (batch == 0) return BWTA_OK;  // empty: pointers may be NULL
+  const bool tern = b_mask != nullptr;
+  BWTA_TRY(check_product(a_mask, a_sign, a_alpha, a_nnz, b_mask, tern, b_sign, b_alpha, M, N, K, Y,
+                         y_dtype, ldy, algo));
+  if (batch == 0 || M == 0 || N == 0) return BWTA_OK;
+  bwta::GemmArgs g{a_mask, a_sign, a_alpha, a_nnz, a_batch_rows, b_mask, b_sign, b_alpha,
+                   b_batch_rows, batch, M, N, K, Y, elt(y_dtype), ldy, y_batch_stride};
+  return run_product(g, algo, false, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,345 @@
+// gemm_popcount.hip - the same binary x ternary products on the vector ALUs
+// with population counts, and the decode GEMV.
+//
+// BWTA page ("BWTA: Accurate and Efficient Binarized Transformer by
+// Algorithm-Hardware Co-design"), Abstract: bit-packed binary/ternary MatMul.
+// With t = mask * (1 - 2 sign_a) and s = 1 - 2 w, t*s = mask * (1 - 2 (sign_a ^ w)),
+// so for one 32-bit word
+//   sum t*s = popc(mask) - 2 popc(mask & (sign_a ^ w))
+//           = popc(mask) - 2 popc(bfi(w, mask ^ sign_a, sign_a))
+// (sign_a is a subset of mask), i.e. one v_bfi_b32 and one accumulating
+// v_bcnt_u32_b32 per 32 products, and acc = nnz - 2 * sum_words popc(...).
+// For ternary x ternary (attention Q K^T):
+//   sum tq*tk = popc(mq & mk) - 2 popc(mq & mk & (aq ^ ak)).
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace bwta {
+namespace {
+
+template <int OUT>
+__device__ __forceinline__ void store_out(void* Y, int64_t idx, int acc, float sa, float sb) {
+  if constexpr (OUT == (int)Elt::I32) {
+    reinterpret_cast<int32_t*>(Y)[idx] = acc;
+  } else {
+    const float sc = sa * sb;
+    const float y = (float)acc * sc;
+    if constexpr (OUT == (int)Elt::F32)
+      reinterpret_cast<float*>(Y)[idx] = y;
+    else
+      reinterpret_cast<uint16_t*>(Y)[idx] = f32_to_bf16_rne(y);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMM: block tile 64 (M) x 128 (N), 256 threads, each thread 4 x 8 outputs.
+// k advances in chunks of 16 words (512 k) staged in LDS.  A is staged as
+// (mask ^ sign, sign), B as sign (binary) or (mask, sign) (ternary).
+// ---------------------------------------------------------------------------
+constexpr int PBM = 64, PBN = 128, PKC = 16;  // tile rows, tile cols, words per chunk
+constexpr int PLD = PKC + 4;                  // padded LDS row length in words
+
+template <bool B_TERNARY, int OUT>
+__global__ void __launch_bounds__(256)
+gemm_popcount_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__ a_sign,
+                     const float* __restrict__ a_alpha, const int32_t* __restrict__ a_nnz,
+                     int64_t a_batch_rows, const uint8_t* __restrict__ b_mask,
+                     const uint8_t* __restrict__ b_sign, const float* __restrict__ b_alpha,
+                     int64_t b_batch_rows, int64_t M, int64_t N, int64_t row_bytes, int tiles_n,
+                     void* __restrict__ Y, int64_t ldy, int64_t y_batch_stride) {
+  __shared__ uint32_t sa_p[PBM * PLD], sa_s[PBM * PLD];
+  __shared__ uint32_t sb_s[PBN * PLD];
+  __shared__ uint32_t sb_m[B_TERNARY ? PBN * PLD : 1];
+
+  const int tid = threadIdx.x;
+  const int tn = tid & 15, tm = tid >> 4;
+  const int64_t b = blockIdx.z;
+  const int tile_m = blockIdx.x / tiles_n;
+  const int tile_n = blockIdx.x - tile_m * tiles_n;
+  const int64_t m0 = (int64_t)tile_m * PBM, n0 = (int64_t)tile_n * PBN;
+  const int64_t a_row0 = b * a_batch_rows + m0, b_row0 = b * b_batch_rows + n0;
+  const int64_t words = row_bytes / 4;
+  const uint32_t* A_m = reinterpret_cast<const uint32_t*>(a_mask + a_row0 * row_bytes);
+  const uint32_t* A_s = reinterpret_cast<const uint32_t*>(a_sign + a_row0 * row_bytes);
+  const uint32_t* B_s = reinterpret_cast<const uint32_t*>(b_sign + b_row0 * row_bytes);
+  const uint32_t* B_m =
+      B_TERNARY ? reinterpret_cast<const uint32_t*>(b_mask + b_row0 * row_bytes) : nullptr;
+  const int64_t w_stride = row_bytes / 4;
+
+  int pos[4][8], neg[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pos[i][j] = neg[i][j] = 0;
+
+  for (int64_t k0 = 0; k0 < words; k0 += PKC) {
+    // Stage: A 64 rows x 16 words (4 per thread), B 128 rows x 16 words (8 per thread).
+    for (int e = tid; e < PBM * PKC; e += 256) {
+      const int row = e / PKC, w = e - row * PKC;
+      const bool ok = m0 + row < M && k0 + w < words;
+      const uint32_t mm = ok ? A_m[row * w_stride + k0 + w] : 0u;
+      const uint32_t ss = ok ? A_s[row * w_stride + k0 + w] : 0u;
+      sa_p[row * PLD + w] = B_TERNARY ? mm : (mm ^ ss);
+      sa_s[row * PLD + w] = ss;
+    }
+    for (int e = tid; e < PBN * PKC; e += 256) {
+      const int row = e / PKC, w = e - row * PKC;
+      const bool ok = n0 + row < N && k0 + w < words;
+      sb_s[row * PLD + w] = ok ? B_s[row * w_stride + k0 + w] : 0u;
+      if constexpr (B_TERNARY) sb_m[row * PLD + w] = ok ? B_m[row * w_stride + k0 + w] : 0u;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int w0 = 0; w0 < PKC; w0 += 4) {
+      uint4 ap[4], as[4], bs[8], bm[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ap[i] = *reinterpret_cast<const uint4*>(&sa_p[(4 * tm + i) * PLD + w0]);
+        as[i] = *reinterpret_cast<const uint4*>(&sa_s[(4 * tm + i) * PLD + w0]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        bs[j] = *reinterpret_cast<const uint4*>(&sb_s[(tn + 16 * j) * PLD + w0]);
+        if constexpr (B_TERNARY) bm[j] = *reinterpret_cast<const uint4*>(&sb_m[(tn + 16 * j) * PLD + w0]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t pa[4] = {ap[i].x, ap[i].y, ap[i].z, ap[i].w};
+          const uint32_t sa[4] = {as[i].x, as[i].y, as[i].z, as[i].w};
+          const uint32_t sw[4] = {bs[j].x, bs[j].y, bs[j].z, bs[j].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if constexpr (B_TERNARY) {
+              const uint32_t mw[4] = {bm[j].x, bm[j].y, bm[j].z, bm[j].w};
+              const uint32_t both = pa[q] & mw[q];  // pa holds the A mask here
+              pos[i][j] += __builtin_popcount(both);
+              neg[i][j] += __builtin_popcount(both & (sa[q] ^ sw[q]));
+            } else {
+              neg[i][j] += __builtin_popcount((sw[q] & pa[q]) | (~sw[q] & sa[q]));
+            }
+          }
+        }
+    }
+    __syncthreads();
+  }
+
+  // Epilogue.  Thread (tm, tn) owns rows 4 tm + i and columns tn + 16 j.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + 4 * tm + i;
+    if (m >= M) continue;
+    const int nz = B_TERNARY ? 0 : a_nnz[b * a_batch_rows + m];
+    const float sa = OUT == (int)Elt::I32 ? 0.0f : a_alpha[b * a_batch_rows + m];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t n = n0 + tn + 16 * j;
+      if (n >= N) continue;
+      const int acc = B_TERNARY ? pos[i][j] - 2 * neg[i][j] : nz - 2 * neg[i][j];
+      const float sb = OUT == (int)Elt::I32 ? 0.0f : b_alpha[b * b_batch_rows + n];
+      store_out<OUT>(Y, b * y_batch_stride + m * ldy + n, acc, sa, sb);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMV (M <= 16): one wave streams whole weight rows; lane l covers bytes
+// [16 l + 1024 c, +16) of every row for chunks c < NCH, so each wave-wide load
+// is one contiguous 1 KiB run, and the activation words it meets are the same
+// for every row: they stay in registers.  MB activation rows are handled per
+// pass.  R rows are accumulated per lane before one reduce-scatter across the
+// wave (integer sums, exact in any order).
+// ---------------------------------------------------------------------------
+template <int V>
+__device__ __forceinline__ void wave_reduce_scatter_int(int (&v)[V]) {
+  // After this, lane l holds in v[0] the wave total of value index bitrev(l mod V).
+  const int lane = __lane_id();
+  int s = 0;
+#pragma unroll
+  for (int cnt = V; cnt > 1; cnt >>= 1, ++s) {
+    const bool hi = (lane >> s) & 1;
+#pragma unroll
+    for (int j = 0; j < cnt / 2; ++j) {
+      const int keep = hi ? v[j + cnt / 2] : v[j];
+      const int send = hi ? v[j] : v[j + cnt / 2];
+      v[j] = keep + __shfl_xor(send, 1 << s, kWave);
+    }
+  }
+#pragma unroll
+  for (int b = s; b < 6; ++b) v[0] += __shfl_xor(v[0], 1 << b, kWave);
+}
+
+template <int BITS>
+__device__ __forceinline__ int bitrev(int x) {
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) r |= ((x >> i) & 1) << (BITS - 1 - i);
+  return r;
+}
+
+template <int MB, int NCH, int R, int OUT>
+__global__ void __launch_bounds__(256)
+gemv_popcount_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__ a_sign,
+                     const float* __restrict__ a_alpha, const int32_t* __restrict__ a_nnz,
+                     int m_base, int m_count, const uint8_t* __restrict__ w_sign,
+                     const float* __restrict__ w_alpha, int64_t N, int64_t row_bytes,
+                     void* __restrict__ Y, int64_t ldy) {
+  constexpr int V = R * MB;
+  constexpr int LOGV = V == 1 ? 0 : V == 2 ? 1 : V == 4 ? 2 : V == 8 ? 3 : V == 16 ? 4 : 5;
+  static_assert((1 << LOGV) == V, "R * MB must be a power of two <= 32");
+  const int lane = __lane_id();
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
+
+  // Activation words of this lane's chunks: p = mask ^ sign, s = sign.
+  uint32_t ap[MB][NCH][4], as[MB][NCH][4];
+  bool cvalid[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int64_t off = (int64_t)c * 1024 + lane * 16;
+    cvalid[c] = off < row_bytes;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const bool ok = cvalid[c] && m < m_count;
+      const int64_t row = m_base + (m < m_count ? m : 0);
+      uint4 mm = ok ? *reinterpret_cast<const uint4*>(a_mask + row * row_bytes + off) : uint4{0, 0, 0, 0};
+      uint4 ss = ok ? *reinterpret_cast<const uint4*>(a_sign + row * row_bytes + off) : uint4{0, 0, 0, 0};
+      ap[m][c][0] = mm.x ^ ss.x; ap[m][c][1] = mm.y ^ ss.y;
+      ap[m][c][2] = mm.z ^ ss.z; ap[m][c][3] = mm.w ^ ss.w;
+      as[m][c][0] = ss.x; as[m][c][1] = ss.y; as[m][c][2] = ss.z; as[m][c][3] = ss.w;
+    }
+  }
+  int nz[MB];
+  float sa[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int64_t row = m_base + (m < m_count ? m : 0);
+    nz[m] = a_nnz[row];
+    sa[m] = OUT == (int)Elt::I32 ? 0.0f : a_alpha[row];
+  }
+
+  for (int64_t n0 = wave * R; n0 < N; n0 += nwaves * R) {
+    int cnt[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) cnt[i] = 0;
+    u32x4 w[R][NCH];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int64_t n = n0 + r < N ? n0 + r : N - 1;
+        w[r][c] = cvalid[c] ? load_nt16(w_sign + n * row_bytes + (int64_t)c * 1024 + lane * 16)
+                            : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t ww[4] = {w[r][c].x, w[r][c].y, w[r][c].z, w[r][c].w};
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            cnt[r * MB + m] += __builtin_popcount((ww[q] & ap[m][c][q]) | (~ww[q] & as[m][c][q]));
+      }
+    wave_reduce_scatter_int<V>(cnt);
+    if (lane < V) {
+      const int v = bitrev<LOGV>(lane);
+      const int r = v / MB, m = v - r * MB;
+      const int64_t n = n0 + r;
+      if (n < N && m < m_count) {
+        const float sb = OUT == (int)Elt::I32 ? 0.0f : w_alpha[n];
+        // select sa[m] without dynamic register indexing
+        float sam = sa[0];
+#pragma unroll
+        for (int mm = 1; mm < MB; ++mm) sam = m == mm ? sa[mm] : sam;
+        int nzm = nz[0];
+#pragma unroll
+        for (int mm = 1; mm < MB; ++mm) nzm = m == mm ? nz[mm] : nzm;
+        store_out<OUT>(Y, (int64_t)(m_base + m) * ldy + n, nzm - 2 * cnt[0], sam, sb);
+      }
+    }
+  }
+}
+
+template <int OUT>
+hipError_t launch_gemm_pc_out(const GemmArgs& g, hipStream_t stream) {
+  const int64_t row_bytes = (g.K + 63) / 64 * 8;
+  const int64_t tm = (g.M + PBM - 1) / PBM, tn = (g.N + PBN - 1) / PBN;
+  const dim3 grid((unsigned)(tm * tn), 1, (unsigned)g.batch), block(256);
+  if (g.b_mask)
+    hipLaunchKernelGGL((gemm_popcount_kernel<true, OUT>), grid, block, 0, stream, g.a_mask, g.a_sign,
+                       g.a_alpha, g.a_nnz, g.a_batch_rows, g.b_mask, g.b_sign, g.b_alpha,
+                       g.b_batch_rows, g.M, g.N, row_bytes, (int)tn, g.Y, g.ldy, g.y_batch_stride);
+  else
+    hipLaunchKernelGGL((gemm_popcount_kernel<false, OUT>), grid, block, 0, stream, g.a_mask,
+                       g.a_sign, g.a_alpha, g.a_nnz, g.a_batch_rows, g.b_mask, g.b_sign, g.b_alpha,
+                       g.b_batch_rows, g.M, g.N, row_bytes, (int)tn, g.Y, g.ldy, g.y_batch_stride);
+  return hipGetLastError();
+}
+
+template <int MB, int NCH, int OUT>
+hipError_t launch_gemv_cfg(const GemmArgs& g, int m_base, int m_count, hipStream_t stream) {
+  constexpr int R = MB >= 4 ? 4 : 8 / MB;
+  const int64_t row_bytes = (g.K + 63) / 64 * 8;
+  const int64_t waves_needed = (g.N + R - 1) / R;
+  int64_t blocks = (waves_needed + 3) / 4;
+  const int64_t cap = 256 * 8;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL((gemv_popcount_kernel<MB, NCH, R, OUT>), dim3((unsigned)blocks), dim3(256), 0,
+                     stream, g.a_mask, g.a_sign, g.a_alpha, g.a_nnz, m_base, m_count, g.b_sign,
+                     g.b_alpha, g.N, row_bytes, g.Y, g.ldy);
+  return hipGetLastError();
+}
+
+template <int NCH, int OUT>
+hipError_t launch_gemv_nch(const GemmArgs& g, hipStream_t stream) {
+  // activation registers: 8 * MB * NCH <= 128
+  constexpr int MBMAX = 16 / NCH >= 4 ? 4 : (16 / NCH >= 2 ? 2 : 1);
+  for (int64_t m0 = 0; m0 < g.M; m0 += MBMAX) {
+    const int cnt = (int)(g.M - m0 < MBMAX ? g.M - m0 : MBMAX);
+    hipError_t e;
+    if (cnt == 1)
+      e = launch_gemv_cfg<1, NCH, OUT>(g, (int)m0, 1, stream);
+    else if (cnt == 2 || MBMAX == 2)
+      e = launch_gemv_cfg<(MBMAX >= 2 ? 2 : 1), NCH, OUT>(g, (int)m0, cnt, stream);
+    else
+      e = launch_gemv_cfg<MBMAX, NCH, OUT>(g, (int)m0, cnt, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int OUT>
+hipError_t launch_gemv_out(const GemmArgs& g, hipStream_t stream) {
+  const int64_t row_bytes = (g.K + 63) / 64 * 8;
+  const int64_t nch = (row_bytes + 1023) / 1024;
+  if (nch <= 1) return launch_gemv_nch<1, OUT>(g, stream);
+  if (nch <= 2) return launch_gemv_nch<2, OUT>(g, stream);
+  if (nch <= 4) return launch_gemv_nch<4, OUT>(g, stream);
+  if (nch <= 8) return launch_gemv_nch<8, OUT>(g, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_popcount(const GemmArgs& g, hipStream_t stream) {
+  switch (g.y_dt) {
+    case Elt::F32: return launch_gemm_pc_out<(int)Elt::F32>(g, stream);
+    case Elt::BF16: return launch_gemm_pc_out<(int)Elt::BF16>(g, stream);
+    case Elt::I32: return launch_gemm_pc_out<(int)Elt::I32>(g, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv_popcount(const GemmArgs& g, hipStream_t stream) {
+  switch (g.y_dt) {
+    case Elt::F32: return launch_gemv_out<(int)Elt::F32>(g, stream);
+    case Elt::BF16: return launch_gemv_out<(int)Elt::BF16>(g, stream);
+    case Elt::I32: return launch_gemv_out<(int)Elt::I32>(g, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace bwta

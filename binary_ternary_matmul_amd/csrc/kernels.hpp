@@ -1,0 +1,44 @@
+// kernels.hpp - host-side launchers of the libbwta kernels (internal).
+//
+// Arguments reach these functions already validated by bwta_api.cpp; each
+// launcher only chooses a kernel configuration and enqueues it on `stream`.
+// They return hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bwta {
+
+enum class Elt : int { F32 = 0, BF16 = 1, I32 = 2 };
+
+// Row reduction + bit packing (ternarize_pack and pack_weights).
+hipError_t launch_ternarize(const void* X, Elt dt, int64_t rows, int64_t K, int64_t stride_row,
+                            uint8_t* mask, uint8_t* sign, float* alpha, int32_t* nnz,
+                            hipStream_t stream);
+hipError_t launch_binarize(const void* W, Elt dt, int64_t rows, int64_t K, int64_t stride_row,
+                           int64_t stride_k, uint8_t* sign, float* alpha, hipStream_t stream);
+
+// Common description of one (possibly batched) product.
+struct GemmArgs {
+  const uint8_t* a_mask;
+  const uint8_t* a_sign;
+  const float* a_alpha;
+  const int32_t* a_nnz;
+  int64_t a_batch_rows;
+  const uint8_t* b_mask;  // nullptr: binary B
+  const uint8_t* b_sign;
+  const float* b_alpha;
+  int64_t b_batch_rows;
+  int64_t batch, M, N, K;
+  void* Y;
+  Elt y_dt;
+  int64_t ldy, y_batch_stride;
+};
+
+hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_gemm_popcount(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_gemv_popcount(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_gemv_mfma(const GemmArgs& g, hipStream_t stream);
+
+}  // namespace bwta

@@ -1,0 +1,163 @@
+/*
+ * bwta.h - C ABI of libbwta.so, the binary-weight x ternary-activation (BWTA)
+ * matrix-product library for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of "BWTA: Accurate and Efficient Binarized Transformer
+ * by Algorithm-Hardware Co-design" (Ding, Liu, Jin, Guo, Lu), Abstract: weights
+ * are binary, activations are ternary with tiny values projected to zero, both
+ * are bit-packed (one bit per weight, two per activation), and binary/ternary
+ * MatMuls serve the linear and the attention operators.  The page fixes no
+ * threshold, scale or reduction order; this library defines them as follows.
+ *
+ * Definitions (every call below computes exactly these; all float operations
+ * are IEEE-754 binary32, round to nearest even, no fused multiply-add):
+ *
+ *   tree(v[0..n))  perfect pairwise tree over v zero-padded to the next power
+ *                  of two P >= n: each level replaces (L[2i], L[2i+1]) by
+ *                  L[2i] + L[2i+1].
+ *   binarize       s[k] = (w[k] < 0) ? -1 : +1   (so -0.0 and +0.0 give +1)
+ *                  alpha_w = tree(|w|) / K
+ *   ternarize      mu = tree(|x|) / K;  thr = 0.5f * mu
+ *                  t[k] = (|x[k]| <= thr) ? 0 : (x[k] < 0 ? -1 : +1)
+ *                  nnz = #{k : t[k] != 0}
+ *                  alpha_a = nnz ? tree(t[k] != 0 ? |x[k]| : 0) / nnz : 0
+ *   product        acc[m][n] = sum_k a[m][k] * b[n][k]  (int32, exact)
+ *   epilogue       y = (float)acc * (alpha_a[m] * alpha_b[n]);  bf16 output is
+ *                  y rounded to nearest even; int32 output is acc itself.
+ *   Divisions are correctly rounded; bf16 inputs widen exactly to fp32.
+ *
+ * Packed bit planes (the only persistent format):
+ *   Kp = round_up(K, 64), row_bytes = Kp / 8.  A plane is row-major, one row of
+ *   row_bytes bytes per matrix row; byte b, bit j (LSB = 0) holds k = 8b + j,
+ *   and bits k >= K are 0.  Little-endian 32/64-bit views of the same bytes hold
+ *   k = 32w + j / 64w + j.
+ *   Binary matrix: one "sign" plane, bit = 1 where the value is -1.
+ *   Ternary matrix: a "mask" plane (bit = 1 where t != 0) and a "sign" plane
+ *   (bit = 1 where t = -1); sign is a subset of mask.
+ *
+ * Memory and streams:
+ *   Every pointer argument except `stream` is device memory owned by the
+ *   caller; the library allocates nothing and keeps no per-call state.  Outputs
+ *   must not alias inputs.  `stream` is a hipStream_t (NULL = the default
+ *   stream); all work is enqueued on it and no call synchronizes.
+ *
+ * Errors:
+ *   Arguments are validated on the host before anything is enqueued:
+ *   BWTA_ERR_INVALID for a NULL required pointer, K <= 0, a negative size, a
+ *   leading dimension smaller than the row, or an unknown dtype/algo;
+ *   BWTA_ERR_ALIGN for a plane pointer that is not 16-byte aligned or a
+ *   float/int pointer that is not aligned to its element; BWTA_ERR_UNSUPPORTED
+ *   for a valid request outside what this build implements (say M > 16 for
+ *   bwta_gemv, or K > BWTA_MAX_K).  A call with zero rows, columns or batch
+ *   entries is a no-op that returns BWTA_OK once sizes, dtypes and algo are
+ *   checked; its pointers are not examined and may be NULL.  A failed launch
+ *   returns BWTA_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *   synchronization.  bwta_last_error() returns a thread-local description of
+ *   the last failure.  No C++ exception crosses this interface.
+ */
+#ifndef BWTA_H_
+#define BWTA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BWTA_API_VERSION 1
+/* Largest K (reduction length) any call accepts. */
+#define BWTA_MAX_K 65536
+
+typedef enum {
+  BWTA_OK = 0,
+  BWTA_ERR_INVALID = 1,
+  BWTA_ERR_ALIGN = 2,
+  BWTA_ERR_UNSUPPORTED = 3,
+  BWTA_ERR_HIP = 4
+} bwta_status;
+
+typedef enum { BWTA_F32 = 0, BWTA_BF16 = 1, BWTA_I32 = 2 } bwta_dtype;
+
+/* Kernel family for the products.  AUTO picks the fastest; MFMA expands the
+ * bit planes to int8 {-1, 0, +1} and multiplies on the int8 matrix cores with
+ * int32 accumulation; POPCOUNT evaluates
+ *   acc = nnz - 2 * sum_words popcount((w & (mask ^ sign)) | (~w & sign))
+ * on the vector ALUs. */
+typedef enum { BWTA_ALGO_AUTO = 0, BWTA_ALGO_MFMA = 1, BWTA_ALGO_POPCOUNT = 2 } bwta_algo;
+
+int bwta_version(void);
+
+/* round_up(K, 64) and round_up(K, 64) / 8; 0 for K <= 0. */
+int64_t bwta_padded_k(int64_t K);
+int64_t bwta_row_bytes(int64_t K);
+
+/* Binary weights (page: Abstract, binary weights at one bit per value).
+ * W: element (r, k) at W[r * stride_row + k * stride_k] (element strides),
+ *    dtype BWTA_F32 or BWTA_BF16; rows >= 0, 0 < K <= BWTA_MAX_K.
+ *    stride_k = 1 is the row-major fast path; stride_row = 1 with
+ *    stride_k = ld packs the columns of a row-major [K, rows] matrix, which is
+ *    how V^T is packed per channel for attention.
+ * sign: out, rows * row_bytes(K) bytes, 16-byte aligned.
+ * alpha: out, rows floats, alpha[r] = tree(|W[r, :]|) / K. */
+bwta_status bwta_pack_weights(const void* W, bwta_dtype w_dtype, int64_t rows, int64_t K,
+                              int64_t stride_row, int64_t stride_k, uint8_t* sign,
+                              float* alpha, void* stream);
+
+/* Ternary activations, projected online (page: Abstract, ternary activations
+ * with tiny values projected to zero, two bits per value).
+ * X: rows x K, row r at X + r * stride_row elements, unit stride along k,
+ *    dtype BWTA_F32 or BWTA_BF16.
+ * mask, sign: out, rows * row_bytes(K) bytes each, 16-byte aligned.
+ * alpha: out, rows floats; nnz: out, rows int32. */
+bwta_status bwta_ternarize_pack(const void* X, bwta_dtype x_dtype, int64_t rows, int64_t K,
+                                int64_t stride_row, uint8_t* mask, uint8_t* sign, float* alpha,
+                                int32_t* nnz, void* stream);
+
+/* Prefill linear (page: Abstract, binary/ternary MatMul for linear operators):
+ * Y[m][n] = epilogue(sum_k t[m][k] * s[n][k]) for a ternary A [M x K] (a_mask,
+ * a_sign, a_alpha, a_nnz as written by bwta_ternarize_pack) and a binary
+ * W [N x K] (w_sign, w_alpha as written by bwta_pack_weights).
+ * Y: M x N, row-major with leading dimension ldy >= N (elements), dtype
+ *    BWTA_F32, BWTA_BF16 or BWTA_I32 (raw accumulators; a_alpha and w_alpha
+ *    may then be NULL). */
+bwta_status bwta_gemm(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
+                      const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha,
+                      int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype, int64_t ldy,
+                      bwta_algo algo, void* stream);
+
+/* Decode GEMV / skinny GEMM, 1 <= M <= 16: the same product as bwta_gemm with
+ * kernels that stream the packed weights from HBM once (page: Abstract, lower
+ * memory footprint; the replies quoted on the page name prefill and decode as
+ * the workloads).  M > 16 returns BWTA_ERR_UNSUPPORTED. */
+bwta_status bwta_gemv(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
+                      const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha,
+                      int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype, int64_t ldy,
+                      bwta_algo algo, void* stream);
+
+/* Batched products for attention (page: Abstract, binary/ternary MatMul for
+ * attention operators).  For b in [0, batch):
+ *   A_b = rows [b * a_batch_rows, b * a_batch_rows + M) of the ternary planes
+ *         a_mask/a_sign (and of a_alpha, a_nnz);
+ *   B_b = rows [b * b_batch_rows, b * b_batch_rows + N) of B; B is ternary
+ *         (b_mask, b_sign) when b_mask != NULL - ternary x ternary, as in
+ *         Q K^T - and binary (b_sign only) when b_mask == NULL - as in P V with
+ *         V^T packed per channel;
+ *   Y_b = Y + b * y_batch_stride elements, M x N with leading dimension ldy.
+ * The epilogue scales by a_alpha[row] * b_alpha[col] unless y_dtype is
+ * BWTA_I32 (raw scores). */
+bwta_status bwta_batched_gemm(int64_t batch, const uint8_t* a_mask, const uint8_t* a_sign,
+                              const float* a_alpha, const int32_t* a_nnz, int64_t a_batch_rows,
+                              const uint8_t* b_mask, const uint8_t* b_sign, const float* b_alpha,
+                              int64_t b_batch_rows, int64_t M, int64_t N, int64_t K, void* Y,
+                              bwta_dtype y_dtype, int64_t ldy, int64_t y_batch_stride,
+                              bwta_algo algo, void* stream);
+
+const char* bwta_status_string(bwta_status status);
+const char* bwta_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BWTA_H_ */

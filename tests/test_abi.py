@@ -1,0 +1,138 @@
+"""The C ABI of libbwta.so on the CPU: the library loads, exports every entry
+point declared in include/bwta.h, and rejects bad arguments with the documented
+status codes before anything reaches the GPU (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bwta.h")
+
+OK, INVALID, ALIGN, UNSUPPORTED, HIPERR = range(5)
+A = 0x10000          # a 16-byte aligned fake device address (never dereferenced)
+MIS = 0x10004        # 4-byte aligned, not 16
+
+
+@pytest.fixture(scope="module")
+def L():
+    from binary_ternary_matmul_amd import _binding, build
+    if not os.path.exists(_binding.LIB_PATH):
+        build.build()
+    return _binding.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bwta_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), f"libbwta.so does not export {n}"
+
+
+def test_version_and_sizes(L):
+    assert L.bwta_version() == 1
+    for K, kp in [(1, 64), (64, 64), (65, 128), (768, 768), (11008, 11008), (100, 128)]:
+        assert L.bwta_padded_k(K) == kp
+        assert L.bwta_row_bytes(K) == kp // 8
+    assert L.bwta_padded_k(0) == 0 and L.bwta_row_bytes(-5) == 0
+
+
+def test_status_strings(L):
+    for s, name in enumerate(["BWTA_OK", "BWTA_ERR_INVALID", "BWTA_ERR_ALIGN",
+                              "BWTA_ERR_UNSUPPORTED", "BWTA_ERR_HIP"]):
+        assert L.bwta_status_string(s).decode() == name
+
+
+def gemm(L, fn="bwta_gemm", **kw):
+    args = dict(a_mask=A, a_sign=A, a_alpha=A, a_nnz=A, w_sign=A, w_alpha=A, M=4, N=4, K=64,
+                Y=A, y_dtype=0, ldy=4, algo=0)
+    args.update(kw)
+    f = getattr(L, fn)
+    return f(*[ctypes.c_void_p(args[k]) if k in ("a_mask", "a_sign", "a_alpha", "a_nnz", "w_sign",
+                                                  "w_alpha", "Y") else args[k]
+               for k in ["a_mask", "a_sign", "a_alpha", "a_nnz", "w_sign", "w_alpha", "M", "N",
+                         "K", "Y", "y_dtype", "ldy", "algo"]], ctypes.c_void_p(0))
+
+
+@pytest.mark.parametrize("fn", ["bwta_gemm", "bwta_gemv"])
+def test_product_validation(L, fn):
+    assert gemm(L, fn, a_mask=0) == INVALID
+    assert gemm(L, fn, w_sign=0) == INVALID
+    assert gemm(L, fn, a_nnz=0) == INVALID
+    assert gemm(L, fn, Y=0) == INVALID
+    assert gemm(L, fn, K=0) == INVALID
+    assert gemm(L, fn, K=-3) == INVALID
+    assert gemm(L, fn, M=-1) == INVALID
+    assert gemm(L, fn, ldy=3) == INVALID
+    assert gemm(L, fn, y_dtype=7) == INVALID
+    assert gemm(L, fn, algo=9) == INVALID
+    assert gemm(L, fn, a_mask=MIS) == ALIGN
+    assert gemm(L, fn, w_sign=A + 8) == ALIGN
+    assert gemm(L, fn, a_alpha=A + 2) == ALIGN
+    assert gemm(L, fn, Y=A + 1) == ALIGN
+    assert gemm(L, fn, K=65537) == UNSUPPORTED
+    assert b"K" in L.bwta_last_error()
+    # empty products are a successful no-op, NULL pointers included
+    assert gemm(L, fn, M=0) == OK
+    assert gemm(L, fn, M=0, a_mask=0, Y=0) == OK
+    assert gemm(L, fn, N=0, ldy=0) == OK
+    # raw int32 output does not need the scales
+    assert gemm(L, fn, a_alpha=0, w_alpha=0, y_dtype=2, M=0) == OK
+
+
+def test_gemv_rejects_m_above_16(L):
+    assert gemm(L, "bwta_gemv", M=17) == UNSUPPORTED
+    assert b"16" in L.bwta_last_error()
+
+
+def test_pack_validation(L):
+    P = ctypes.c_void_p
+    f = L.bwta_pack_weights
+    assert f(P(0), 0, 4, 64, 64, 1, P(A), P(A), P(0)) == INVALID
+    assert f(P(A), 5, 4, 64, 64, 1, P(A), P(A), P(0)) == INVALID
+    assert f(P(A), 0, 4, 0, 64, 1, P(A), P(A), P(0)) == INVALID
+    assert f(P(A), 0, 4, 64, 64, 0, P(A), P(A), P(0)) == INVALID
+    assert f(P(A), 0, 4, 64, 64, 1, P(MIS), P(A), P(0)) == ALIGN
+    assert f(P(A + 2), 0, 4, 64, 64, 1, P(A), P(A), P(0)) == ALIGN
+    assert f(P(A + 2), 1, 0, 64, 64, 1, P(A), P(A), P(0)) == OK      # bf16: 2-byte aligned is fine
+    assert f(P(A), 0, 0, 64, 64, 1, P(A), P(A), P(0)) == OK          # zero rows
+    assert f(P(0), 0, 0, 64, 64, 1, P(0), P(0), P(0)) == OK          # zero rows, NULL pointers
+    t = L.bwta_ternarize_pack
+    assert t(P(A), 0, 4, 64, 64, P(A), P(A), P(A), P(0), P(0)) == INVALID   # nnz NULL
+    assert t(P(A), 0, 4, 64, 32, P(A), P(A), P(A), P(A), P(0)) == INVALID   # stride < K
+    assert t(P(A), 0, 4, 70000, 70000, P(A), P(A), P(A), P(A), P(0)) == UNSUPPORTED
+    assert t(P(A), 0, 4, 64, 64, P(A), P(MIS), P(A), P(A), P(0)) == ALIGN
+    assert t(P(A), 0, 0, 64, 64, P(A), P(A), P(A), P(A), P(0)) == OK
+
+
+def test_batched_validation(L):
+    P = ctypes.c_void_p
+    f = L.bwta_batched_gemm
+
+    def call(batch=2, b_mask=A, a_nnz=A, ab=4, bb=4, M=4, N=4, K=64, ldy=4, ys=16, dt=2):
+        return f(batch, P(A), P(A), P(A), P(a_nnz), ab, P(b_mask), P(A), P(A), bb, M, N, K, P(A),
+                 dt, ldy, ys, 0, P(0))
+    assert call(batch=-1) == INVALID
+    assert call(ab=-1) == INVALID
+    assert call(b_mask=MIS) == ALIGN
+    assert call(batch=70000) == UNSUPPORTED
+    assert call(batch=0) == OK
+    # empty batch: a no-op before any pointer is examined
+    assert call(a_nnz=0, b_mask=0, batch=0) == OK
+    # ternary x ternary does not use nnz; binary B does
+    assert call(a_nnz=0, b_mask=0, M=0) == OK
+    assert call(a_nnz=0, b_mask=0, K=0) == INVALID
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    from binary_ternary_matmul_amd import bwta_ternarize_pack
+    with pytest.raises(ValueError):
+        bwta_ternarize_pack(torch.zeros(4, 64))

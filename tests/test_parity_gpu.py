@@ -1,0 +1,229 @@
+"""GPU parity: every libbwta kernel against the CPU oracle on the same seeded
+inputs, at sizes that span several tiles and end in ragged tails.
+
+Bar: packed planes, nnz and int32 accumulators bit-exact; alpha bit-exact (the
+same pairwise tree); fp32 outputs within a relative error of 1e-5 (they are
+expected to be bit-exact, since both sides evaluate fl32(acc * fl32(aa * ab)));
+bf16 outputs equal after round-to-nearest-even.
+"""
+import numpy as np
+import pytest
+
+from binary_ternary_matmul_amd import inputs
+from tests.helpers import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def bw():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import binary_ternary_matmul_amd as b
+    b.lib()
+    return b
+
+
+def _x(seed, M, K, bf16, nu=4.0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = inputs.student_t(rng, (M, K), nu)
+    x, _ = inputs.with_outlier_channels(x, rng, max(1, K // 100), 20.0)
+    # a few exact zeros, signed zeros and a fully-zero row
+    x[0, :: max(1, K // 7)] = 0.0
+    if M > 2:
+        x[2, :] = 0.0
+    if M > 3:
+        x[3, 1::3] = -0.0
+    return inputs.f32_to_bf16_bits(x) if bf16 else x
+
+
+def _w(seed, N, K, bf16=False):
+    rng = np.random.Generator(np.random.PCG64(seed + 7))
+    w = inputs.normal(rng, (N, K), 0.02)
+    w[0, ::5] = 0.0
+    if N > 1:
+        w[1, ::3] = -0.0
+    return inputs.f32_to_bf16_bits(w) if bf16 else w
+
+
+def assert_close_f32(got, ref):
+    ref = ref.astype(np.float64)
+    err = np.abs(got.astype(np.float64) - ref)
+    bad = err > REL_TOL * np.abs(ref)
+    assert not bad.any(), f"{bad.sum()} outputs beyond rel 1e-5; worst {err.max()}"
+
+
+# ----------------------------------------------------------------------------
+# ternarize_pack
+# ----------------------------------------------------------------------------
+TERN_SHAPES = [(1, 1), (3, 3), (5, 64), (7, 65), (9, 100), (33, 128), (17, 256), (16, 768),
+               (12, 1000), (8, 2048), (6, 3072), (5, 4096), (4, 4097), (3, 11008), (2, 28672),
+               (2, 65536)]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("M,K", TERN_SHAPES)
+def test_ternarize_pack(bw, oracle, M, K, bf16):
+    x = _x(100 + K, M, K, bf16)
+    got = bw.bwta_ternarize_pack(to_dev(x))
+    t, alpha, nnz = oracle.ternarize(x)
+    assert (to_host(got.mask) == oracle.pack_plane(t, "mask")).all()
+    assert (to_host(got.sign) == oracle.pack_plane(t, "sign")).all()
+    assert (to_host(got.nnz) == nnz).all()
+    assert (to_host(got.alpha).view(np.uint32) == alpha.view(np.uint32)).all()
+
+
+def test_ternarize_pack_row_stride(bw, oracle):
+    import torch
+    x = _x(5, 40, 300, False)
+    big = np.zeros((40, 320), np.float32)
+    big[:, :300] = x
+    got = bw.bwta_ternarize_pack(to_dev(big)[:, :300])
+    t, alpha, nnz = oracle.ternarize(x)
+    assert (to_host(got.mask) == oracle.pack_plane(t, "mask")).all()
+    assert (to_host(got.sign) == oracle.pack_plane(t, "sign")).all()
+    assert (to_host(got.alpha) == alpha).all() and (to_host(got.nnz) == nnz).all()
+    del torch
+
+
+# ----------------------------------------------------------------------------
+# pack_weights
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("N,K", [(1, 1), (3, 7), (70, 64), (33, 100), (130, 768), (9, 4096),
+                                 (5, 11008), (3, 28672)])
+def test_pack_weights(bw, oracle, N, K, bf16):
+    w = _w(N * 31 + K, N, K, bf16)
+    got = bw.bwta_pack_weights(to_dev(w))
+    s, alpha = oracle.binarize(w)
+    assert (to_host(got.sign) == oracle.pack_plane(s, "sign")).all()
+    assert (to_host(got.alpha).view(np.uint32) == alpha.view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("L,C", [(2048, 128), (100, 70), (64, 1)])
+def test_pack_weights_columns(bw, oracle, L, C, bf16):
+    """V^T packing: the columns of a row-major [L, C] matrix become rows."""
+    v = _w(L + C, L, C, bf16)
+    got = bw.bwta_pack_weights(to_dev(v), transpose=True)
+    s, alpha = oracle.binarize(v, transpose=True)
+    assert (to_host(got.sign) == oracle.pack_plane(s, "sign")).all()
+    assert (to_host(got.alpha) == alpha).all()
+
+
+# ----------------------------------------------------------------------------
+# products
+# ----------------------------------------------------------------------------
+GEMM_SHAPES = [(1, 1, 1), (5, 3, 64), (17, 33, 65), (128, 128, 256), (130, 260, 200),
+               (257, 129, 1000), (128, 768, 768), (300, 130, 4096), (64, 300, 11008),
+               (200, 100, 28672 + 64)]
+
+
+def _linear_case(oracle, M, N, K, bf16=False):
+    x = _x(M * 1000 + N + K, M, K, bf16)
+    w = _w(M + N * 7 + K, N, K)
+    ref = oracle.linear(x, w, out="bf16")
+    return x, w, ref
+
+
+@pytest.mark.parametrize("algo", ["mfma", "popcount"])
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm(bw, oracle, M, N, K, algo):
+    x, w, ref = _linear_case(oracle, M, N, K)
+    a = bw.bwta_ternarize_pack(to_dev(x))
+    wp = bw.bwta_pack_weights(to_dev(w))
+    acc = to_host(bw.bwta_gemm(a, wp, out_dtype="i32", algo=algo))
+    assert (acc == ref["acc"]).all(), f"{(acc != ref['acc']).sum()} accumulators differ"
+    y = to_host(bw.bwta_gemm(a, wp, out_dtype="f32", algo=algo))
+    assert_close_f32(y, ref["y"])
+    assert (y.view(np.uint32) == ref["y"].view(np.uint32)).all()
+    yb = to_host(bw.bwta_gemm(a, wp, out_dtype="bf16", algo=algo))
+    assert (yb == ref["y_bf16"]).all()
+
+
+def test_gemm_ldy(bw, oracle):
+    import torch
+    M, N, K = 70, 90, 300
+    x, w, ref = _linear_case(oracle, M, N, K)
+    a = bw.bwta_ternarize_pack(to_dev(x))
+    wp = bw.bwta_pack_weights(to_dev(w))
+    for algo in ["mfma", "popcount"]:
+        out = torch.full((M, 100), -7.0, device="cuda")
+        bw.bwta_gemm(a, wp, out_dtype="f32", algo=algo, out=out)
+        o = to_host(out)
+        assert (o[:, :N] == ref["y"]).all() and (o[:, N:] == -7.0).all()
+
+
+@pytest.mark.parametrize("algo", ["popcount", "mfma", "auto"])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("N,K", [(1000, 1024), (513, 8192), (300, 28672), (77, 200)])
+def test_gemv(bw, oracle, M, N, K, algo):
+    x, w, ref = _linear_case(oracle, M, N, K, bf16=True)
+    a = bw.bwta_ternarize_pack(to_dev(x))
+    wp = bw.bwta_pack_weights(to_dev(w))
+    acc = to_host(bw.bwta_gemv(a, wp, out_dtype="i32", algo=algo))
+    assert (acc == ref["acc"]).all()
+    y = to_host(bw.bwta_gemv(a, wp, out_dtype="f32", algo=algo))
+    assert (y.view(np.uint32) == ref["y"].view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("algo", ["mfma", "popcount"])
+@pytest.mark.parametrize("H,L,D", [(3, 130, 128), (2, 257, 64), (4, 256, 100)])
+def test_batched_ternary_ternary(bw, oracle, H, L, D, algo):
+    rng = np.random.Generator(np.random.PCG64(H * L + D))
+    q = inputs.f32_to_bf16_bits(rng.standard_normal((H * L, D), dtype=np.float32))
+    k = inputs.f32_to_bf16_bits(rng.standard_normal((H * L, D), dtype=np.float32) * 1.5)
+    qa = bw.bwta_ternarize_pack(to_dev(q))
+    ka = bw.bwta_ternarize_pack(to_dev(k))
+    got = to_host(bw.bwta_batched_gemm(H, qa, L, ka, L, L, L, out_dtype="i32", algo=algo))
+    tq, _, _ = oracle.ternarize(q)
+    tk, _, _ = oracle.ternarize(k)
+    for h in range(H):
+        ref = oracle.matmul_i32(tq[h * L:(h + 1) * L], tk[h * L:(h + 1) * L])
+        assert (got[h] == ref).all(), f"head {h}"
+
+
+@pytest.mark.parametrize("algo", ["mfma", "popcount"])
+@pytest.mark.parametrize("H,L,D", [(2, 300, 128), (3, 256, 64)])
+def test_batched_ternary_binary(bw, oracle, H, L, D, algo):
+    """P V: ternary P [L, L] per head times binary V^T [D, L] per head."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(H + L + D))
+    P = rng.dirichlet(np.ones(L), size=H * L).astype(np.float32)         # rows sum to 1
+    V = inputs.f32_to_bf16_bits(rng.standard_normal((H, L, D), dtype=np.float32))
+    pa = bw.bwta_ternarize_pack(to_dev(P))
+    vt_sign = torch.empty((H * D, bw.row_bytes(L)), dtype=torch.uint8, device="cuda")
+    vt_alpha = torch.empty(H * D, dtype=torch.float32, device="cuda")
+    Vd = to_dev(V)
+    for h in range(H):
+        vp = bw.bwta_pack_weights(Vd[h], transpose=True)
+        vt_sign[h * D:(h + 1) * D] = vp.sign
+        vt_alpha[h * D:(h + 1) * D] = vp.alpha
+    vb = bw.BinaryPlanes(vt_sign, vt_alpha, L)
+    got = to_host(bw.bwta_batched_gemm(H, pa, L, vb, D, L, D, out_dtype="f32", algo=algo))
+    tp, ap, _ = oracle.ternarize(P)
+    for h in range(H):
+        s, av = oracle.binarize(V[h], transpose=True)
+        acc = oracle.matmul_i32(tp[h * L:(h + 1) * L], s)
+        ref = oracle.scale(acc, ap[h * L:(h + 1) * L], av)
+        assert (got[h].view(np.uint32) == ref.view(np.uint32)).all(), f"head {h}"
+
+
+def test_empty_and_degenerate(bw, oracle):
+    import torch
+    # zero rows: no-op
+    X = torch.zeros((0, 64), device="cuda")
+    got = bw.bwta_ternarize_pack(X)
+    assert got.mask.shape == (0, 8)
+    # all-zero activations: every output is 0
+    x = np.zeros((5, 200), np.float32)
+    w = _w(1, 9, 200)
+    a = bw.bwta_ternarize_pack(to_dev(x))
+    wp = bw.bwta_pack_weights(to_dev(w))
+    assert (to_host(a.nnz) == 0).all() and (to_host(a.alpha) == 0).all()
+    for algo in ["mfma", "popcount"]:
+        assert (to_host(bw.bwta_gemm(a, wp, algo=algo)) == 0).all()
+        assert (to_host(bw.bwta_gemv(a, wp, algo=algo)) == 0).all()
