@@ -1,0 +1,338 @@
+"""Benchmark of the binary-weight x ternary-activation hot path on one MI355X.
+
+One step = one LLaMA-7B-shaped decoder layer's linears at prefill (M = 2048
+tokens): ternarize+pack the four bf16 activation inputs (attention input,
+attention output, MLP input, MLP activation) and run the seven binary x ternary
+GEMMs (q, k, v, o: 4096 -> 4096; gate, up: 4096 -> 11008; down: 11008 -> 4096)
+with the fused bf16 epilogue.  Weights are packed once before timing (as for a
+deployed model).  `value` is the step's int8-equivalent throughput in TOPS
+(2*M*N*K over the seven GEMMs per step time, ternarize included).
+
+The same run also measures, each in its own object on the JSON line:
+  gemv       decode GEMV/skinny GEMM, LLaMA2-70B shapes, M in {1, 4, 16}: HBM GB/s
+             with >= 20 rotating weight copies so every launch reads from HBM
+  attention  32 heads x 2048 x 128: ternarize Q, K -> Q K^T (int32 scores) and
+             ternarize P -> pack V^T -> P V
+  popcount   the VALU popcount GEMM on the same seven GEMMs (the alternative to MFMA)
+  bert       BERT-base encoder linears, M = 4096, fp32 in, bf16 out
+  roofline   the MFMA GEMM kernel's achieved int8 TOPS against the dense int8 peak
+  cpu_baseline  the scalar CPU oracle on a bounded row sample of the same step
+
+Inputs are synthetic (seeded generators in binary_ternary_matmul_amd.inputs).
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POPS
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(x):
+    import torch
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def graph_of(fn, reps=1, warm=2):
+    """Capture `reps` back-to-back calls of fn (all launches on torch's current
+    stream) into one HIP graph.  Many calls per graph amortise the graph-launch
+    overhead, which on this stack is several microseconds per replay."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(warm):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps_inside, replays=3):
+    """Milliseconds per captured call: HIP events around `replays` replays of a
+    graph holding `reps_inside` calls."""
+    import torch
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(replays):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / (replays * reps_inside)
+
+
+def time_calls(fn, reps=20, replays=3):
+    return time_graph(graph_of(fn, reps), reps, replays)
+
+
+def bench_prefill(bw, steps, warmup, M=2048):
+    import torch
+    from binary_ternary_matmul_amd import inputs
+    acts, lins = inputs.llama7b_prefill(M)
+    log(f"[prefill] generating inputs M={M}")
+    X = {name: dev(gen()) for name, gen in acts.items()}
+    W = {}
+    for lin in lins:
+        W[lin.name] = bw.bwta_pack_weights(dev(lin.w()))
+    torch.cuda.synchronize()
+    outs = {lin.name: torch.empty((M, lin.N), dtype=torch.bfloat16, device="cuda") for lin in lins}
+    ops = sum(2.0 * M * lin.N * lin.K for lin in lins)
+
+    def ternarize_all():
+        return {name: bw.bwta_ternarize_pack(x) for name, x in X.items()}
+
+    def gemms(planes):
+        for lin in lins:
+            a = planes[inputs.LLAMA7B_INPUTS[lin.name]]
+            bw.bwta_gemm(a, W[lin.name], "bf16", "mfma", outs[lin.name])
+
+    def step():
+        gemms(ternarize_all())
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # The timed region is one HIP graph holding exactly `steps` steps: the same
+    # kernels the eager calls launch, without per-launch host overhead.
+    g_steps = graph_of(step, reps=steps)
+    torch.cuda.synchronize()
+    s_ev = torch.cuda.Event(enable_timing=True)
+    e_ev = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s_ev.record()
+    g_steps.replay()
+    e_ev.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = s_ev.elapsed_time(e_ev) / steps
+    # GEMM-only time (the dominant kernel) and a per-GEMM breakdown.
+    planes = ternarize_all()
+    gemm_ms = time_calls(lambda: gemms(planes), reps=steps)
+    per_gemm = {}
+    for lin in lins:
+        a = planes[inputs.LLAMA7B_INPUTS[lin.name]]
+        ms = time_calls(lambda a=a, lin=lin: bw.bwta_gemm(a, W[lin.name], "bf16", "mfma",
+                                                          outs[lin.name]), reps=steps)
+        per_gemm[lin.name] = {"M": M, "N": lin.N, "K": lin.K, "us": round(ms * 1e3, 2),
+                              "tops": round(2.0 * M * lin.N * lin.K / (ms * 1e-3) / 1e12, 1)}
+    tern_ms = time_calls(ternarize_all, reps=steps)
+    return dict(ops=ops, ms_step=ms_step, wall_ms_step=wall * 1e3 / steps, gemm_ms=gemm_ms,
+                ternarize_ms=tern_ms, per_gemm=per_gemm, lins=lins, X=X, W=W, M=M)
+
+
+def bench_popcount(bw, pre, reps=5):
+    import torch
+    from binary_ternary_matmul_amd import inputs
+    planes = {name: bw.bwta_ternarize_pack(x) for name, x in pre["X"].items()}
+    res = {}
+    tot_ops, tot_ms = 0.0, 0.0
+    for lin in pre["lins"]:
+        a = planes[inputs.LLAMA7B_INPUTS[lin.name]]
+        out = torch.empty((pre["M"], lin.N), dtype=torch.bfloat16, device="cuda")
+        ms = time_calls(lambda a=a, lin=lin: bw.bwta_gemm(a, pre["W"][lin.name], "bf16", "popcount",
+                                                          out), reps=reps)
+        ops = 2.0 * pre["M"] * lin.N * lin.K
+        tot_ops += ops
+        tot_ms += ms
+        res[lin.name] = {"us": round(ms * 1e3, 1), "tops": round(ops / (ms * 1e-3) / 1e12, 1)}
+    return {"layer_tops": round(tot_ops / (tot_ms * 1e-3) / 1e12, 1),
+            "mfma_speedup_over_popcount": round(tot_ms / pre["gemm_ms"], 2), "per_gemm": res}
+
+
+def bench_gemv(bw, copies=24, reps=4):
+    """Decode: HBM GB/s with rotating packed-weight copies (> 512 MB per shape)."""
+    import torch
+    from binary_ternary_matmul_amd import inputs
+    out = {}
+    for M in (1, 4, 16):
+        for lin in inputs.llama70b_decode(M):
+            if M == 1:
+                log(f"[gemv] packing {lin.name} {lin.N}x{lin.K}")
+                w = bw.bwta_pack_weights(dev(lin.w()))
+                torch.cuda.synchronize()
+                ws = [w] + [bw.BinaryPlanes(w.sign.clone(), w.alpha.clone(), w.K)
+                            for _ in range(copies - 1)]
+                out.setdefault("_w", {})[lin.name] = ws
+            ws = out["_w"][lin.name]
+            a = bw.bwta_ternarize_pack(dev(lin.x()))
+            y = torch.empty((M, lin.N), dtype=torch.float32, device="cuda")
+
+            def run_all(a=a, y=y, ws=ws):
+                for wi in ws:
+                    bw.bwta_gemv(a, wi, "f32", "auto", y)
+            ms = time_calls(run_all, reps=reps)
+            us = ms * 1e3 / len(ws)
+            kp = bw.padded_k(lin.K)
+            nbytes = lin.N * kp / 8 + 4 * lin.N + M * (2 * kp / 8 + 8) + 4 * M * lin.N
+            gbs = nbytes / (us * 1e-6) / 1e9
+            out[f"{lin.name}_M{M}"] = {"N": lin.N, "K": lin.K, "us": round(us, 2),
+                                       "bytes": int(nbytes), "GBps": round(gbs, 1),
+                                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 3)}
+    out.pop("_w", None)
+    return out
+
+
+def bench_attention(bw, reps=5, H=32, L=2048, D=128):
+    import torch
+    from binary_ternary_matmul_amd import inputs
+    att = inputs.attention(H, L, D)
+    Q = dev(att.q.reshape(H * L, D))
+    Kt = dev(att.k.reshape(H * L, D))
+    # V as [L, H*D] (tokens x all heads' channels): one launch packs V^T of every
+    # head, plane row h*D + d = channel d of head h.
+    Vf = dev(np.ascontiguousarray(att.v.transpose(1, 0, 2).reshape(L, H * D)))
+    scores = torch.empty((H, L, L), dtype=torch.int32, device="cuda")
+    O = torch.empty((H, L, D), dtype=torch.float32, device="cuda")
+    # P for timing: softmax of the scaled scores, computed once on the GPU with torch
+    qa = bw.bwta_ternarize_pack(Q)
+    ka = bw.bwta_ternarize_pack(Kt)
+    bw.bwta_batched_gemm(H, qa, L, ka, L, L, L, "i32", "auto", scores)
+    z = scores.float() * (qa.alpha.view(H, L, 1) * ka.alpha.view(H, 1, L)) / (D ** 0.5)
+    P = torch.softmax(z, dim=-1).reshape(H * L, L).contiguous()
+    del z
+    torch.cuda.synchronize()
+
+    def qk():
+        a = bw.bwta_ternarize_pack(Q)
+        b = bw.bwta_ternarize_pack(Kt)
+        bw.bwta_batched_gemm(H, a, L, b, L, L, L, "i32", "auto", scores)
+
+    def pv():
+        pa = bw.bwta_ternarize_pack(P)
+        vb = bw.bwta_pack_weights(Vf, transpose=True)
+        bw.bwta_batched_gemm(H, pa, L, vb, D, L, D, "f32", "auto", O)
+
+    ms_qk = time_calls(qk, reps=reps)
+    ms_pv = time_calls(pv, reps=reps)
+    ops = 2.0 * H * L * L * D
+    return {"heads": H, "L": L, "d": D,
+            "qk_ms": round(ms_qk, 3), "qk_scores_GBps": round(H * L * L * 4 / (ms_qk * 1e-3) / 1e9, 1),
+            "pv_ms": round(ms_pv, 3), "pv_tops_incl_ternarize_P": round(ops / (ms_pv * 1e-3) / 1e12, 1)}
+
+
+def bench_bert(bw, reps=10):
+    import torch
+    from binary_ternary_matmul_amd import inputs
+    lins = inputs.bert_encoder()
+    tot_ops, tot_ms = 0.0, 0.0
+    res = {}
+    for lin in lins:
+        x = dev(lin.x())
+        w = bw.bwta_pack_weights(dev(lin.w()))
+        y = torch.empty((lin.M, lin.N), dtype=torch.bfloat16, device="cuda")
+        ms = time_calls(lambda x=x, w=w, y=y: bw.bwta_gemm(bw.bwta_ternarize_pack(x), w, "bf16",
+                                                           "auto", y), reps=reps)
+        ops = 2.0 * lin.M * lin.N * lin.K
+        tot_ops += ops
+        tot_ms += ms
+        res[lin.name] = {"us": round(ms * 1e3, 1), "tops": round(ops / (ms * 1e-3) / 1e12, 1)}
+    return {"layer_tops_incl_ternarize": round(tot_ops / (tot_ms * 1e-3) / 1e12, 1), "per_gemm": res}
+
+
+def cpu_baseline(M=2048, rows=384):
+    """The oracle, untouched, on the first `rows` token rows of the same step."""
+    from binary_ternary_matmul_amd import inputs
+    from oracle import oracle
+    acts, lins = inputs.llama7b_prefill(M)
+    xs = {name: gen()[:rows] for name, gen in acts.items()}
+    ws = [(lin, oracle.binarize(lin.w())[0]) for lin in lins]   # weights are packed offline
+    threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    ts = {name: oracle.ternarize(x)[0] for name, x in xs.items()}
+    ops = 0.0
+    for lin, s in ws:
+        oracle.matmul_i32(ts[inputs.LLAMA7B_INPUTS[lin.name]], s, threads=threads)
+        ops += 2.0 * rows * lin.N * lin.K
+    dt = time.perf_counter() - t0
+    return {"value": round(ops / dt / 1e12, 4), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"ternarize + dense int32 product of the first {rows} of {M} token rows "
+                      f"of all seven LLaMA-7B layer GEMMs ({ops / 1e9:.0f} G ops)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--quick", action="store_true", help="prefill step only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import binary_ternary_matmul_amd as bw
+    bw.lib()
+
+    pre = bench_prefill(bw, args.steps, args.warmup)
+    achieved = pre["ops"] / (pre["gemm_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": "binary×ternary GEMM TOPS (% int8 MFMA peak); decode GEMV HBM GB/s",
+        "value": round(pre["ops"] / (pre["ms_step"] * 1e-3) / 1e12, 1),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": "llama7b_prefill_layer_linears", "tokens": pre["M"],
+                   "gemms": {k: [v["M"], v["N"], v["K"]] for k, v in pre["per_gemm"].items()},
+                   "activations": "bf16 Student-t(3), 1% outlier channels x50",
+                   "weights": "N(0,0.02) packed to 1 bit", "out": "bf16",
+                   "ops_per_step": pre["ops"]},
+        "gemm_frac_of_int8_peak": round(achieved / INT8_PEAK_TOPS, 3),
+        "ternarize_us_per_step": round(pre["ternarize_ms"] * 1e3, 1),
+        "host_wall_ms_per_step": round(pre["wall_ms_step"], 4),
+        "per_gemm": pre["per_gemm"],
+        "roofline": {"bound": "mfma", "kernel": "gemm_mfma_kernel", "achieved": round(achieved, 1),
+                     "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / INT8_PEAK_TOPS, 3), "traffic": None},
+    }
+    if not args.quick:
+        log("[bench] popcount variant")
+        line["popcount"] = bench_popcount(bw, pre)
+        log("[bench] gemv")
+        line["gemv"] = bench_gemv(bw)
+        log("[bench] attention")
+        line["attention"] = bench_attention(bw)
+        log("[bench] bert")
+        line["bert"] = bench_bert(bw)
+    if not args.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -161,6 +161,10 @@ static bwta_status run_product(const bwta::GemmArgs& g, bwta_algo algo, bool gem
       e = bwta::launch_gemv_popcount(g, stream);
     else
       e = bwta::launch_gemm_popcount(g, stream);
+  } else if (g.K <= 64) {
+    // One 64-bit word per row: below the MFMA kernel's 16-byte DMA window;
+    // the popcount kernel computes the same exact sums.
+    e = bwta::launch_gemm_popcount(g, stream);
   } else {
     e = bwta::launch_gemm_mfma(g, stream);
   }

@@ -69,11 +69,14 @@ __device__ __forceinline__ float wave_tree(const float (&in)[N]) {
   int s = 0;
 #pragma unroll
   for (int cnt = N; cnt > 1; cnt >>= 1, ++s) {
-    const bool hi = (lane >> s) & 1;
+    // all-ones when this lane keeps the upper half; the halves are blended
+    // bitwise (a select here gets rewritten into a runtime register index)
+    const uint32_t hi = 0u - (uint32_t)((lane >> s) & 1);
 #pragma unroll
     for (int j = 0; j < cnt / 2; ++j) {
-      const float keep = hi ? v[j + cnt / 2] : v[j];
-      const float send = hi ? v[j] : v[j + cnt / 2];
+      const uint32_t lo_b = __float_as_uint(v[j]), up_b = __float_as_uint(v[j + cnt / 2]);
+      const float keep = __uint_as_float((lo_b & ~hi) | (up_b & hi));
+      const float send = __uint_as_float((up_b & ~hi) | (lo_b & hi));
       const float recv = __shfl_xor(send, 1 << s, kWave);
       v[j] = keep + recv;
     }

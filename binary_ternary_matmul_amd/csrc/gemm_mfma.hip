@@ -1,5 +1,5 @@
 // gemm_mfma.hip - binary x ternary and ternary x ternary products on the int8
-// matrix cores of gfx950 (v_mfma_i32_16x16x64_i8, int32 accumulation).
+// matrix cores of gfx950 (v_mfma_i32_32x32x32_i8, int32 accumulation).
 //
 // BWTA page ("BWTA: Accurate and Efficient Binarized Transformer by
 // Algorithm-Hardware Co-design"), Abstract: a binary/ternary MatMul for the
@@ -8,15 +8,16 @@
 // rescaled by alpha_a[m] * alpha_b[n] in the fused epilogue.
 //
 // Design (gfx950 first, not the page's CUDA kernel):
-// * One wave owns a 128 x 128 output tile (8 x 8 MFMA tiles of 16 x 16, 256
-//   int32 accumulators per lane, held in AGPRs at one wave per SIMD).
-// * Operands stay packed until the last moment: each lane loads 64-bit words of
-//   the mask/sign planes straight from global memory (L2-resident: a tile's
-//   packed operands are 1/8 - 1/4 of their int8 size) and expands them in
-//   registers directly into the MFMA operand layout.  No LDS is used for
-//   operands.  The k order inside an MFMA is free as long as A and B use the
-//   same one; lane group g = lane/16 takes the 64-bit word g of each 256-bit
-//   step, and dword d (0..7) of a 32-bit word holds in byte j the bit 8j + d.
+// * One wave owns a 128 x 128 output tile (4 x 4 MFMA tiles of 32 x 32, 256
+//   int32 accumulators per lane, held in AGPRs at one wave per SIMD; the
+//   32 x 32 form keeps the register allocator from splitting them).
+// * Operands stay packed until the last moment: the packed bit planes of each
+//   256-k step (32 bytes per row) are copied global -> LDS with direct 16-byte
+//   DMA loads, double-buffered per wave, and each lane expands the words it
+//   needs from LDS in registers directly into the MFMA operand layout.  The k
+//   order inside an MFMA is free as long as A and B use the same one: lane
+//   group g = lane/32 takes 64-bit words 2g and 2g+1 of the step, and dword d
+//   (0..7) of a 32-bit word holds in byte j the bit 8j + d.
 // * Expansion uses v_perm_b32 as a byte lookup (selector 0..7 picks a byte of
 //   the 8-byte table, 12 gives 0x00, >= 13 gives 0xFF, 8 copies the sign of
 //   byte 1):
@@ -35,9 +36,10 @@ namespace bwta {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int TILES = 8;            // 16-row MFMA tiles per wave along M and along N
-constexpr int WAVE_TILE = 16 * TILES;
+constexpr int TILES = 4;            // 32-row MFMA tiles per wave along M and along N
+constexpr int WAVE_TILE = 32 * TILES;
 
 // v_perm tables: __builtin_amdgcn_perm(hi, lo, sel) reads bytes 0..3 from lo
 // and 4..7 from hi.
@@ -76,10 +78,12 @@ __device__ __forceinline__ uint64_t ld64(const uint8_t* p) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Packed words of one step held by a lane: words 2g and 2g+1 of the rows
+// 32t + r of each plane.
 template <bool B_TERNARY>
 struct Packed {
-  uint64_t am[TILES], as[TILES];
-  uint64_t bm[B_TERNARY ? TILES : 1], bs[TILES];
+  uint64_t am[TILES][2], as[TILES][2];
+  uint64_t bm[B_TERNARY ? TILES : 1][2], bs[TILES][2];
 };
 
 // LDS staging of one step (256 k = 32 bytes of each of 128 rows per plane).
@@ -91,27 +95,35 @@ struct Stage {
   static constexpr int kBytes = kPlane * kPlanes;
 };
 
-// Copy 32 bytes of each of 128 rows of one plane into LDS with direct
-// global->LDS 16-byte loads: lane i of instruction j moves half (i & 1) of row
-// 32j + i/2, and the hardware stores lane i's 16 bytes at dst + 16 i, so row
-// rho lands at dst + 32 rho.  Rows past `valid` reuse the last valid row (their
-// results are never stored).  Only full steps (32 bytes inside the row) come
-// here.
-__device__ __forceinline__ void dma_plane(const uint8_t* __restrict__ plane, int64_t row_bytes,
-                                          int valid, int64_t st, uint8_t* dst, int lane) {
+// Copy 32 bytes (one 256-k step) of each of 128 rows of one plane into LDS
+// with direct global->LDS 16-byte loads: lane i of instruction j moves half
+// (i & 1) of row 32j + i/2, and the hardware stores lane i's 16 bytes at
+// dst + 16 i, so row rho lands at dst + 32 rho.  Every source stays inside the
+// matrix:
+// * rows past `valid` reuse the last valid row (their results are never stored);
+// * a half that starts past the row end reads the row start instead (its words
+//   are zeroed when the stage is read);
+// * a half that straddles the row end (row_bytes % 16 == 8) reads the 16 bytes
+//   that end at the row end, so the row's last word lands one word later in
+//   the stage than its position; read_stage compensates.  This needs
+//   row_bytes >= 16 (K > 64), which the launcher guarantees.
+// The address is a wave-uniform base plus a 32-bit lane offset.
+__device__ __forceinline__ void dma_plane(const uint8_t* __restrict__ plane, uint32_t row_bytes,
+                                          int valid, uint32_t st, uint8_t* dst, int lane) {
+  uint32_t o = st * 32 + (lane & 1) * 16;
+  if (o + 16 > row_bytes) o = o < row_bytes ? row_bytes - 16 : 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    int rho = 32 * j + (lane >> 1);
-    rho = rho < valid ? rho : valid - 1;
-    const uint8_t* src = plane + (int64_t)rho * row_bytes + st * 32 + (lane & 1) * 16;
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + j * 1024), 16, 0, 0);
+    const int rho = min(32 * j + (lane >> 1), valid - 1);
+    __builtin_amdgcn_global_load_lds(plane + ((uint32_t)rho * row_bytes + o),
+                                     (lds_void_t*)(dst + j * 1024), 16, 0, 0);
   }
 }
 
 template <bool B_TERNARY>
 __device__ __forceinline__ void dma_step(const uint8_t* am, const uint8_t* as, const uint8_t* bm,
-                                         const uint8_t* bs, int64_t row_bytes, int m_valid,
-                                         int n_valid, int64_t st, uint8_t* stage, int lane) {
+                                         const uint8_t* bs, uint32_t row_bytes, int m_valid,
+                                         int n_valid, uint32_t st, uint8_t* stage, int lane) {
   constexpr int P = Stage<B_TERNARY>::kPlane;
   dma_plane(am, row_bytes, m_valid, st, stage, lane);
   dma_plane(as, row_bytes, m_valid, st, stage + P, lane);
@@ -119,68 +131,72 @@ __device__ __forceinline__ void dma_step(const uint8_t* am, const uint8_t* as, c
   if constexpr (B_TERNARY) dma_plane(bm, row_bytes, n_valid, st, stage + 3 * P, lane);
 }
 
-// Lane (r, g) reads 64-bit word g of row 16t + r of each plane.
+// Lane (r, g) reads 64-bit words 2g, 2g+1 of row 32t + r of each plane with one
+// 16-byte LDS read.  `shift`: the row's last word straddled the DMA window and
+// sits one slot late (it is word 2g, found in slot 2g+1).  Words past the row
+// end are zeroed on the A side, which zeroes their products whatever B holds.
 template <bool B_TERNARY>
 __device__ __forceinline__ void read_stage(Packed<B_TERNARY>& p, const uint8_t* stage, int r,
-                                           int g) {
+                                           int g, bool shift, bool k0in, bool k1in) {
   constexpr int P = Stage<B_TERNARY>::kPlane;
+  typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int t = 0; t < TILES; ++t) {
-    const int off = (16 * t + r) * 32 + 8 * g;
-    p.am[t] = *reinterpret_cast<const uint64_t*>(stage + off);
-    p.as[t] = *reinterpret_cast<const uint64_t*>(stage + P + off);
-    p.bs[t] = *reinterpret_cast<const uint64_t*>(stage + 2 * P + off);
-    if constexpr (B_TERNARY) p.bm[t] = *reinterpret_cast<const uint64_t*>(stage + 3 * P + off);
-  }
-}
-
-// Partial last step (the row ends inside it): plain bounded loads.
-template <bool B_TERNARY>
-__device__ __forceinline__ void load_direct(Packed<B_TERNARY>& p, const uint8_t* __restrict__ am,
-                                            const uint8_t* __restrict__ as,
-                                            const uint8_t* __restrict__ bm,
-                                            const uint8_t* __restrict__ bs, int64_t row_bytes,
-                                            int64_t words, int64_t kw, int m_valid, int n_valid,
-                                            int r) {
-  const bool kin = kw < words;
-#pragma unroll
-  for (int t = 0; t < TILES; ++t) {
-    const int ra = 16 * t + r < m_valid ? 16 * t + r : m_valid - 1;
-    const int rb = 16 * t + r < n_valid ? 16 * t + r : n_valid - 1;
-    const int64_t oa = (int64_t)ra * row_bytes + kw * 8;
-    const int64_t ob = (int64_t)rb * row_bytes + kw * 8;
-    p.am[t] = kin ? ld64(am + oa) : 0ull;
-    p.as[t] = kin ? ld64(as + oa) : 0ull;
-    p.bs[t] = kin ? ld64(bs + ob) : 0ull;
-    if constexpr (B_TERNARY) p.bm[t] = kin ? ld64(bm + ob) : 0ull;
-  }
-}
-
-template <bool B_TERNARY>
-__device__ __forceinline__ void compute_step(const Packed<B_TERNARY>& p, v4i (&acc)[TILES][TILES]) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      v4i a[TILES], b[TILES];
-#pragma unroll
-      for (int t = 0; t < TILES; ++t)
-        a[t] = expand_ternary((uint32_t)(p.am[t] >> (32 * h)), (uint32_t)(p.as[t] >> (32 * h)), q);
-#pragma unroll
-      for (int t = 0; t < TILES; ++t) {
-        if constexpr (B_TERNARY)
-          b[t] = expand_ternary((uint32_t)(p.bm[t] >> (32 * h)), (uint32_t)(p.bs[t] >> (32 * h)), q);
-        else
-          b[t] = expand_binary((uint32_t)(p.bs[t] >> (32 * h)), q);
-      }
-#pragma unroll
-      for (int i = 0; i < TILES; ++i)
-#pragma unroll
-        for (int j = 0; j < TILES; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+    const int off = (32 * t + r) * 32 + 16 * g;
+    const u64x2 m = *reinterpret_cast<const u64x2*>(stage + off);
+    const u64x2 s = *reinterpret_cast<const u64x2*>(stage + P + off);
+    const u64x2 w = *reinterpret_cast<const u64x2*>(stage + 2 * P + off);
+    p.am[t][0] = k0in ? (shift ? m[1] : m[0]) : 0ull;
+    p.as[t][0] = k0in ? (shift ? s[1] : s[0]) : 0ull;
+    p.am[t][1] = k1in ? m[1] : 0ull;
+    p.as[t][1] = k1in ? s[1] : 0ull;
+    p.bs[t][0] = shift ? w[1] : w[0];
+    p.bs[t][1] = w[1];
+    if constexpr (B_TERNARY) {
+      const u64x2 bm = *reinterpret_cast<const u64x2*>(stage + 3 * P + off);
+      p.bm[t][0] = shift ? bm[1] : bm[0];
+      p.bm[t][1] = bm[1];
     }
   }
 }
+
+// One 256-k step: 8 slices of 32 k per lane group (word w, 32-bit half h,
+// nibble half q).  Per slice the 4 B operands are expanded first, then each A
+// operand right before its 4 MFMAs.
+template <bool B_TERNARY>
+__device__ __forceinline__ void compute_step(const Packed<B_TERNARY>& p,
+                                             v16i (&acc)[TILES][TILES]) {
+#pragma unroll
+  for (int w = 0; w < 2; ++w)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        v4i b[TILES];
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+          if constexpr (B_TERNARY)
+            b[t] = expand_ternary((uint32_t)(p.bm[t][w] >> (32 * h)),
+                                  (uint32_t)(p.bs[t][w] >> (32 * h)), q);
+          else
+            b[t] = expand_binary((uint32_t)(p.bs[t][w] >> (32 * h)), q);
+        }
+#pragma unroll
+        for (int i = 0; i < TILES; ++i) {
+          const v4i a = expand_ternary((uint32_t)(p.am[i][w] >> (32 * h)),
+                                       (uint32_t)(p.as[i][w] >> (32 * h)), q);
+#pragma unroll
+          for (int j = 0; j < TILES; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[j], acc[i][j], 0, 0, 0);
+        }
+      }
+}
+
+// Output tile in LDS: 128 rows of 128 int32, padded by 8 words per row so that
+// the accumulator writes (2 rows x 32 columns per instruction, 4 rows apart)
+// hit 64 distinct banks.
+constexpr int kTileLd = WAVE_TILE + 8;
+constexpr size_t kTileBytes = (size_t)WAVE_TILE * kTileLd * 4;
 
 template <bool B_TERNARY, int OUT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -188,17 +204,24 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
                  const float* __restrict__ a_alpha, int64_t a_batch_rows,
                  const uint8_t* __restrict__ b_mask, const uint8_t* __restrict__ b_sign,
                  const float* __restrict__ b_alpha, int64_t b_batch_rows, int64_t M, int64_t N,
-                 int64_t row_bytes, int tiles_n, void* __restrict__ Y, int64_t ldy,
+                 int64_t row_bytes, int tiles_m, int tiles_n, void* __restrict__ Y, int64_t ldy,
                  int64_t y_batch_stride) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int S = blockDim.x / kWave;
   const int lane = __lane_id();
   const int wid = threadIdx.x / kWave;
-  const int r = lane & 15;
-  const int g = lane >> 4;
+  const int r = lane & 31;
+  const int g = lane >> 5;
 
+  // Blocks are dealt round-robin to the 8 XCDs; give each XCD a contiguous run
+  // of tiles (consecutive tile_n for the same tile_m) so that tiles sharing A
+  // rows share that XCD's L2.
+  const int nblk = tiles_m * tiles_n;
+  int lin = blockIdx.x;
+  if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int tile_m = lin / tiles_n;
+  const int tile_n = lin - tile_m * tiles_n;
   const int64_t b = blockIdx.z;
-  const int tile_m = blockIdx.x / tiles_n;
-  const int tile_n = blockIdx.x - tile_m * tiles_n;
   const int64_t m0 = (int64_t)tile_m * WAVE_TILE;
   const int64_t n0 = (int64_t)tile_n * WAVE_TILE;
   const int m_valid = (int)(M - m0 < WAVE_TILE ? M - m0 : WAVE_TILE);
@@ -216,105 +239,144 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   const int64_t st0 = steps * wid / S;
   const int64_t st1 = steps * (wid + 1) / S;
 
-  v4i acc[TILES][TILES];
+  // The tile's scales go to LDS now; the loads complete behind the main loop
+  // and the epilogue reads them from LDS (made visible by its first barrier).
+  __shared__ float s_alpha_a[WAVE_TILE], s_alpha_b[WAVE_TILE];
+  if constexpr (OUT != (int)Elt::I32) {
+    if (wid == 0) {
+#pragma unroll
+      for (int h = 0; h < WAVE_TILE / kWave; ++h) {
+        const int i = h * kWave + lane;
+        s_alpha_a[i] = i < m_valid ? a_alpha[b * a_batch_rows + m0 + i] : 0.0f;
+        s_alpha_b[i] = i < n_valid ? b_alpha[b * b_batch_rows + n0 + i] : 0.0f;
+      }
+    }
+  }
+
+  v16i acc[TILES][TILES];
 #pragma unroll
   for (int i = 0; i < TILES; ++i)
 #pragma unroll
-    for (int j = 0; j < TILES; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < TILES; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0;
 
-  // Double-buffered LDS stages of this wave; step st+1 is in flight while step
-  // st is expanded and multiplied.  Words past the row end (kw >= words) are
-  // zeroed on the A side, which zeroes their products.
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // Double-buffered LDS stages of this wave: step st+1 is in flight while step
+  // st is expanded and multiplied.
   uint8_t* stages = smem + (size_t)wid * 2 * Stage<B_TERNARY>::kBytes;
-  // Full steps (32 bytes inside every row) go through the DMA pipeline; only
-  // the very last step of a row can be partial, and it is peeled off so that
-  // the loop body never waits on anything but its own stage.
-  const int64_t full_steps = row_bytes / 32;
-  const int64_t fe = st1 < full_steps ? st1 : (st0 > full_steps ? st0 : full_steps);
-  if (st0 < fe) dma_step<B_TERNARY>(am, as, bm, bs, row_bytes, m_valid, n_valid, st0, stages, lane);
-  for (int64_t st = st0; st < fe; ++st) {
+  const uint32_t rb = (uint32_t)row_bytes;
+  const bool straddle = (rb & 15u) == 8u;  // the last word is read one slot late
+  if (st0 < st1) dma_step<B_TERNARY>(am, as, bm, bs, rb, m_valid, n_valid, (uint32_t)st0, stages, lane);
+  for (int64_t st = st0; st < st1; ++st) {
     uint8_t* stage = stages + ((st - st0) & 1) * Stage<B_TERNARY>::kBytes;
     Packed<B_TERNARY> p;
     // vmcnt(0) (expcnt/lgkmcnt fields at their no-wait maxima): the DMA of this
     // step has landed in LDS.
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    read_stage<B_TERNARY>(p, stage, r, g);
-    if (st + 1 < fe)
-      dma_step<B_TERNARY>(am, as, bm, bs, row_bytes, m_valid, n_valid, st + 1,
+    if (st * 4 + 4 <= words) {
+      read_stage<B_TERNARY>(p, stage, r, g, false, true, true);
+    } else {  // the row ends inside this step
+      const int64_t kw = st * 4 + 2 * g;
+      read_stage<B_TERNARY>(p, stage, r, g, straddle && kw == words - 1, kw < words,
+                            kw + 1 < words);
+    }
+    if (st + 1 < st1)
+      dma_step<B_TERNARY>(am, as, bm, bs, rb, m_valid, n_valid, (uint32_t)(st + 1),
                           stages + ((st + 1 - st0) & 1) * Stage<B_TERNARY>::kBytes, lane);
     compute_step<B_TERNARY>(p, acc);
   }
-  for (int64_t st = fe; st < st1; ++st) {  // at most one partial step
-    Packed<B_TERNARY> p;
-    const int64_t kw = st * 4 + g;
-    load_direct<B_TERNARY>(p, am, as, bm, bs, row_bytes, words, kw, m_valid, n_valid, r);
-    compute_step<B_TERNARY>(p, acc);
-  }
 
-  // Exact split-K reduction: waves 1..S-1 hand their tiles to wave 0 in turn
-  // through one 64 KiB LDS slot (int32 addition is associative).
-  v4i* red = reinterpret_cast<v4i*>(smem);
-  if (S > 1) __syncthreads();  // every wave is done with its stages
-  for (int src = 1; src < S; ++src) {
-    if (wid == src) {
-#pragma unroll
-      for (int i = 0; i < TILES; ++i)
-#pragma unroll
-        for (int j = 0; j < TILES; ++j) red[(i * TILES + j) * kWave + lane] = acc[i][j];
-    }
-    __syncthreads();
-    if (wid == 0) {
-#pragma unroll
-      for (int i = 0; i < TILES; ++i)
-#pragma unroll
-        for (int j = 0; j < TILES; ++j) acc[i][j] += red[(i * TILES + j) * kWave + lane];
-    }
-    __syncthreads();
-  }
-  if (wid != 0) return;
-
-  // Epilogue: D[i][j] of a 16x16 tile sits in lane j + 16*(i/4), register i%4.
-  float aa[TILES][4], ab[TILES];
-  if constexpr (OUT != (int)Elt::I32) {
+  // Sum the S partial tiles exactly in one LDS tile (wave 0 stores, the others
+  // add with LDS integer atomics), then let all S waves write the result.
+  // D[i][j] of a 32x32 MFMA tile sits in lane j + 32*((i/4)%2), register
+  // (i%4) + 4*(i/8).
+  int32_t* tile = reinterpret_cast<int32_t*>(smem);
+  __syncthreads();  // every wave is done with its stages
+  if (wid == 0) {
 #pragma unroll
     for (int i = 0; i < TILES; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = 16 * i + 4 * g + q;
-        aa[i][q] = row < m_valid ? a_alpha[a_row0 + row] : 0.0f;
-      }
+      for (int j = 0; j < TILES; ++j)
 #pragma unroll
-    for (int j = 0; j < TILES; ++j) {
-      const int col = 16 * j + r;
-      ab[j] = col < n_valid ? b_alpha[b_row0 + col] : 0.0f;
+        for (int q = 0; q < 16; ++q)
+          tile[(32 * i + (q & 3) + 8 * (q >> 2) + 4 * g) * kTileLd + 32 * j + r] = acc[i][j][q];
+  }
+  if (S > 1) {
+    __syncthreads();
+    if (wid != 0) {
+#pragma unroll
+      for (int i = 0; i < TILES; ++i)
+#pragma unroll
+        for (int j = 0; j < TILES; ++j)
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            atomicAdd(&tile[(32 * i + (q & 3) + 8 * (q >> 2) + 4 * g) * kTileLd + 32 * j + r],
+                      acc[i][j][q]);
     }
   }
+  __syncthreads();
+
+  // Epilogue: each wave takes rows wid, wid + S, ...; a half-wave covers one
+  // 128-column row with 4 columns per lane, so every store is row-contiguous
+  // (one 16- or 8-byte store per lane when the row is aligned and complete).
+  const int half = lane >> 5;
+  const int c4 = (lane & 31) * 4;
+  float ab[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (OUT != (int)Elt::I32) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ab[u] = s_alpha_b[c4 + u];
+  }
+  constexpr int ES = OUT == (int)Elt::BF16 ? 2 : 4;
+  const bool vec_ok = ((ldy * ES) % 16 == 0) && ((y_batch_stride * ES) % 16 == 0) &&
+                      ((n0 * ES) % 16 == 0) && (reinterpret_cast<uintptr_t>(Y) % 16 == 0);
+  const bool full_cols = c4 + 4 <= n_valid;
   char* ybase = static_cast<char*>(Y);
+  for (int row = 2 * wid + half; row < m_valid; row += 2 * S) {
+    const int4 v = *reinterpret_cast<const int4*>(&tile[row * kTileLd + c4]);
+    const int vv[4] = {v.x, v.y, v.z, v.w};
+    const int64_t yoff = b * y_batch_stride + (m0 + row) * ldy + n0 + c4;
+    if constexpr (OUT == (int)Elt::I32) {
+      int32_t* y = reinterpret_cast<int32_t*>(ybase) + yoff;
+      if (vec_ok && full_cols) {
+        *reinterpret_cast<int4*>(y) = v;
+      } else {
 #pragma unroll
-  for (int i = 0; i < TILES; ++i)
+        for (int u = 0; u < 4; ++u)
+          if (c4 + u < n_valid) y[u] = vv[u];
+      }
+    } else {
+      const float aa = s_alpha_a[row];
+      float out[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = 16 * i + 4 * g + q;
-      if (row >= m_valid) continue;
-      const int64_t yrow = b * y_batch_stride + (m0 + row) * ldy + n0;
-#pragma unroll
-      for (int j = 0; j < TILES; ++j) {
-        const int col = 16 * j + r;
-        if (col >= n_valid) continue;
-        const int v = acc[i][j][q];
-        if constexpr (OUT == (int)Elt::I32) {
-          reinterpret_cast<int32_t*>(ybase)[yrow + col] = v;
+      for (int u = 0; u < 4; ++u) {
+        const float sc = aa * ab[u];
+        out[u] = (float)vv[u] * sc;
+      }
+      if constexpr (OUT == (int)Elt::F32) {
+        float* y = reinterpret_cast<float*>(ybase) + yoff;
+        if (vec_ok && full_cols) {
+          *reinterpret_cast<float4*>(y) = make_float4(out[0], out[1], out[2], out[3]);
         } else {
-          const float sc = aa[i][q] * ab[j];
-          const float y = (float)v * sc;
-          if constexpr (OUT == (int)Elt::F32)
-            reinterpret_cast<float*>(ybase)[yrow + col] = y;
-          else
-            reinterpret_cast<uint16_t*>(ybase)[yrow + col] = f32_to_bf16_rne(y);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (c4 + u < n_valid) y[u] = out[u];
+        }
+      } else {
+        uint16_t* y = reinterpret_cast<uint16_t*>(ybase) + yoff;
+        uint16_t h[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) h[u] = f32_to_bf16_rne(out[u]);
+        if (vec_ok && full_cols) {
+          *reinterpret_cast<uint2*>(y) = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                                    (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (c4 + u < n_valid) y[u] = h[u];
         }
       }
     }
+  }
 }
 
 // Split K over S waves when that fills more SIMDs: minimise rounds(S) / S, where a
@@ -345,8 +407,7 @@ hipError_t launch_b(const GemmArgs& g, hipStream_t stream) {
   const dim3 grid((unsigned)(tm * tn), 1, (unsigned)g.batch);
   const dim3 block((unsigned)(S * kWave));
   size_t lds = (size_t)S * 2 * Stage<B_TERNARY>::kBytes;
-  const size_t red_bytes = (size_t)TILES * TILES * kWave * sizeof(v4i);
-  if (S > 1 && lds < red_bytes) lds = red_bytes;
+  if (lds < kTileBytes) lds = kTileBytes;
 #define BWTA_GEMM_LAUNCH(OUT_)                                                                  \
   do {                                                                                          \
     auto kfn = gemm_mfma_kernel<B_TERNARY, OUT_>;                                               \
@@ -355,7 +416,7 @@ hipError_t launch_b(const GemmArgs& g, hipStream_t stream) {
     if (e != hipSuccess) return e;                                                              \
     hipLaunchKernelGGL(kfn, grid, block, lds, stream, g.a_mask, g.a_sign, g.a_alpha,            \
                        g.a_batch_rows, g.b_mask, g.b_sign, g.b_alpha, g.b_batch_rows, g.M, g.N, \
-                       row_bytes, (int)tn, g.Y, g.ldy, g.y_batch_stride);                       \
+                       row_bytes, (int)tm, (int)tn, g.Y, g.ldy, g.y_batch_stride);                       \
   } while (0)
   switch (g.y_dt) {
     case Elt::F32:

@@ -3,90 +3,151 @@
 // BWTA page ("BWTA: Accurate and Efficient Binarized Transformer by
 // Algorithm-Hardware Co-design"), Abstract: activations become ternary by
 // projecting tiny values to zero, weights become binary, and both are
-// bit-packed (Figure 6 shows 32 values packed into one 32-bit word).  The
-// threshold and the scales follow the library definition in bwta.h:
+// bit-packed (Figure 6 packs 32 values into one 32-bit word).  The threshold and
+// the scales follow the library definition in bwta.h:
 //   mu = tree(|x|)/K, thr = 0.5*mu, t = |x| <= thr ? 0 : sign(x),
 //   alpha_a = tree(kept |x|)/nnz;  alpha_w = tree(|w|)/K, s = (w < 0) ? -1 : +1.
 //
-// Layout of the work.  A row is cut into groups of G = 64*V elements, V = 16
-// bytes / element size (4 fp32 or 8 bf16).  In group i lane l owns the V
-// consecutive elements [i*G + l*V, +V), which it reads with one 16-byte load,
-// so every wave-wide load is one contiguous 1 KiB run.  A wave owns GPW
-// consecutive groups (GPW a power of two); W waves share a row when
-// GPW*G*W >= K needs them, and every (lane run, group, wave) block is an aligned
-// power-of-two sub-tree of the tree over the zero-padded row, so
-//   lane tree (V) -> wave tree (64 lanes x GPW groups) -> LDS tree (W waves)
-// reproduces the definition bit for bit.  The row stays in registers between
+// Row kernel.  A row is cut into groups of G = LPR*8 elements; in a group, lane
+// l (of the LPR lanes serving the row) owns the 8 consecutive elements
+// [8l, 8l+8), read with one (bf16) or two (fp32) 16-byte loads, so a wave-wide
+// load is one contiguous run.  Those 8 elements give exactly one byte of each
+// bit plane, which the lane stores itself: no cross-lane bit shuffling.  A wave
+// owns GPW consecutive groups; W waves share a row when one wave is not enough.
+// Every (lane run, group, wave) block is an aligned power-of-two sub-tree of the
+// tree over the zero-padded row, so
+//   lane tree (8) -> wave tree (LPR lanes x GPW groups) -> LDS tree (W waves)
+// reproduces the definition bit for bit.  Small rows (K <= 256) use LPR = 16 or
+// 32 lanes per row, several rows per wave.  The row stays in registers between
 // the two passes (sum, then threshold), so x is read from HBM once.
 //
-// Bits: lane l's V mask/sign bits land at bit offset l*V of its group; lanes are
-// OR-combined with shuffles into 32-bit words (8 lanes of 4 bits for fp32, 4
-// lanes of 8 bits for bf16) and stored as whole words.
+// Column kernel.  Packing the columns of a row-major [K, C] matrix (V^T for
+// attention) gives each lane one column: a wave-wide load reads 64 adjacent
+// columns of one row (contiguous), a lane folds its column's runs of 8 values
+// into the pairwise tree with a register stack (a binary counter over the run
+// index), and W waves split K into aligned power-of-two ranges.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace bwta {
 namespace {
 
+constexpr int RUN = 8;  // elements per lane run = bits per stored plane byte
+
 template <typename T>
-struct Elem;
-template <>
-struct Elem<float> {
-  static constexpr int V = 4;
-  static constexpr int GPW_MAX = 16;
-};
-template <>
-struct Elem<uint16_t> {
-  static constexpr int V = 8;
-  static constexpr int GPW_MAX = 8;
+struct Raw {
+  static constexpr int kWords = RUN * (int)sizeof(T) / 4;  // 32-bit words per run
 };
 
-__device__ __forceinline__ float to_f32(float v) { return v; }
-__device__ __forceinline__ float to_f32(uint16_t v) { return bf16_bits_to_f32(v); }
+// fp32 bit pattern of element j of a run.
+__device__ __forceinline__ uint32_t ebits(const uint32_t* raw, int j, float) { return raw[j]; }
+__device__ __forceinline__ uint32_t ebits(const uint32_t* raw, int j, uint16_t) {
+  return (raw[j >> 1] >> (16 * (j & 1))) << 16;
+}
+__device__ __forceinline__ float elem(const uint32_t* raw, int j, float t) {
+  return __uint_as_float(ebits(raw, j, t));
+}
+__device__ __forceinline__ float elem(const uint32_t* raw, int j, uint16_t t) {
+  return __uint_as_float(ebits(raw, j, t));
+}
 
-// V elements starting at k = e of one row (zeros beyond K).
-template <typename T, bool VEC>
+// Decisions as integer arithmetic on the IEEE bit patterns (finite inputs), so
+// no per-element lane masks are formed.  For non-negative floats a, t:
+// a > t  <=>  bits(a) > bits(t)  <=>  bit 31 of (bits(t) - bits(a)).
+__device__ __forceinline__ uint32_t gt_bit(uint32_t ua, uint32_t ut) { return (ut - ua) >> 31; }
+// x < 0 (so -0.0 counts as non-negative): sign bit set and not exactly -0.0.
+__device__ __forceinline__ uint32_t neg_bit(uint32_t ux) {
+  return (ux >> 31) & ((0x80000000u - ux) >> 31);
+}
+
+__device__ __forceinline__ uint32_t raw_bits(float v) { return __float_as_uint(v); }
+__device__ __forceinline__ uint32_t raw_bits(uint16_t v) { return v; }
+
+// The run of 8 elements starting at k = e of one row, as raw words.
+// MODE 0: the run lies inside the row, unit stride, 16-byte aligned: vector
+//         loads, issued back to back by the caller for all its runs.
+// MODE 1: unit stride, aligned, K a multiple of 8, so a run lies either inside
+//         the row (vector load) or past its end (zeros).
+// MODE 2: any strides (the generic gather): element loads, 64-bit offsets.
+template <typename T, int MODE>
 __device__ __forceinline__ void load_run(const T* __restrict__ row, int64_t e, int64_t K,
-                                         int64_t sk, float (&out)[Elem<T>::V]) {
-  constexpr int V = Elem<T>::V;
-  if (VEC && e + V <= K) {
-    const u32x4 u = load_nt16(row + e);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-    if constexpr (sizeof(T) == 4) {
+                                         int64_t sk, uint32_t (&raw)[Raw<T>::kWords]) {
+  constexpr int NW = Raw<T>::kWords;
+  auto vec = [&](int32_t off) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) out[j] = __uint_as_float(w[j]);
+    for (int v = 0; v < NW / 4; ++v) {
+      const u32x4 u = load_nt16(row + off + v * (16 / sizeof(T)));
+      raw[4 * v + 0] = u.x;
+      raw[4 * v + 1] = u.y;
+      raw[4 * v + 2] = u.z;
+      raw[4 * v + 3] = u.w;
+    }
+  };
+  auto put = [&](int j, uint32_t b) {
+    if constexpr (sizeof(T) == 4)
+      raw[j] = b;
+    else
+      raw[j >> 1] |= b << (16 * (j & 1));
+  };
+  if constexpr (MODE == 0) {
+    vec((int32_t)e);
+  } else if constexpr (MODE == 1) {
+    if (e < K) {
+      vec((int32_t)e);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        out[2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
-        out[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
-      }
+      for (int w = 0; w < NW; ++w) raw[w] = 0u;
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < V; ++j) out[j] = (e + j < K) ? to_f32(row[(e + j) * sk]) : 0.0f;
+    for (int w = 0; w < NW; ++w) raw[w] = 0u;
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) {
+      const int64_t k = e + j < K ? e + j : K - 1;
+      const uint32_t b = raw_bits(row[k * sk]);
+      put(j, e + j < K ? b : 0u);
+    }
   }
 }
 
-// One row (or W rows' worth of waves) per iteration; see the file comment.
-template <typename T, int GPW, bool TERNARY, bool VEC>
-__global__ void __launch_bounds__(1024)
+template <int LPR>
+__device__ __forceinline__ float lanes_tree(float v) {
+  // pairwise over the LPR lanes of one row (lane bit 0 first)
+#pragma unroll
+  for (int b = 1; b < LPR; b <<= 1) v = v + __shfl_xor(v, b, kWave);
+  return v;
+}
+template <int LPR>
+__device__ __forceinline__ int lanes_sum(int v) {
+#pragma unroll
+  for (int b = 1; b < LPR; b <<= 1) v += __shfl_xor(v, b, kWave);
+  return v;
+}
+
+// RELOAD: pass 2 reads each run again (from L2: the block read it moments
+// before) instead of keeping the whole row in registers; used for the wide rows
+// that need 8 or 16 waves per row, where 1024-thread blocks cap registers.
+template <typename T, int GPW, int LPR, bool TERNARY, bool VEC, int BLOCK, bool RELOAD>
+__global__ void __launch_bounds__(BLOCK)
 pack_rows_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t sr, int64_t sk, int W,
                  int64_t row_bytes, uint8_t* __restrict__ mask, uint8_t* __restrict__ sign,
                  float* __restrict__ alpha, int32_t* __restrict__ nnz) {
-  constexpr int V = Elem<T>::V;
-  constexpr int G = kWave * V;
-  constexpr int LPW = 32 / V;  // lanes per 32-bit output word
+  static_assert(LPR == 64 || GPW == 1, "sub-wave rows use one group");
+  constexpr int NW = Raw<T>::kWords;
+  constexpr int G = LPR * RUN;
+  constexpr int RPW = kWave / LPR;  // rows per wave
   __shared__ float red_sum[16];
   __shared__ float red_kept[16];
   __shared__ int red_cnt[16];
 
   const int lane = __lane_id();
   const int wid = threadIdx.x / kWave;
-  const int rpb = (blockDim.x / kWave) / W;
-  const int row_in_block = wid / W;
-  const int w_in_row = wid - row_in_block * W;
-  const int64_t Kp = row_bytes * 8;
+  const int wpb = BLOCK / kWave;
+  const int ll = lane % LPR;
+  // rows handled by the block per iteration, and this lane's row among them
+  const int rpb = LPR == 64 ? wpb / W : wpb * RPW;
+  const int row_in_block = LPR == 64 ? wid / W : wid * RPW + lane / LPR;
+  const int w_in_row = LPR == 64 ? wid - (wid / W) * W : 0;
   const float fK = (float)K;
 
   for (int64_t r0 = (int64_t)blockIdx.x * rpb; r0 < rows; r0 += (int64_t)gridDim.x * rpb) {
@@ -94,15 +155,27 @@ pack_rows_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t sr, i
     const bool live = r < rows;
     const T* xrow = X + (live ? r : 0) * sr;
 
-    float x[GPW][V];
+    uint32_t raw[RELOAD ? 1 : GPW][NW];
+    // wave-uniform: all GPW groups of this wave lie inside the row
+    const bool full = VEC && (int64_t)(w_in_row * GPW + GPW) * G <= K;
+    const int64_t e0 = (int64_t)(w_in_row * GPW) * G + (int64_t)ll * RUN;
+    auto fetch = [&](int i, uint32_t (&dst)[NW]) {
+      if constexpr (VEC) {
+        if (full)
+          load_run<T, 0>(xrow, e0 + i * G, K, 1, dst);
+        else
+          load_run<T, 1>(xrow, e0 + i * G, K, 1, dst);
+      } else {
+        load_run<T, 2>(xrow, e0 + i * G, K, sk, dst);
+      }
+    };
+    if constexpr (!RELOAD) {
+      if (full) {
 #pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-      const int64_t e = (int64_t)(w_in_row * GPW + i) * G + (int64_t)lane * V;
-      if (live) {
-        load_run<T, VEC>(xrow, e, K, sk, x[i]);
+        for (int i = 0; i < GPW; ++i) load_run<T, 0>(xrow, e0 + i * G, K, 1, raw[i]);
       } else {
 #pragma unroll
-        for (int j = 0; j < V; ++j) x[i][j] = 0.0f;
+        for (int i = 0; i < GPW; ++i) fetch(i, raw[i]);
       }
     }
 
@@ -110,53 +183,83 @@ pack_rows_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t sr, i
     float part[GPW];
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
-      float a[V];
+      if constexpr (RELOAD) fetch(i, raw[0]);
+      const uint32_t* rw = raw[RELOAD ? 0 : i];
+      float a[RUN];
 #pragma unroll
-      for (int j = 0; j < V; ++j) a[j] = fabsf(x[i][j]);
-      part[i] = lane_tree<V>(a);
+      for (int j = 0; j < RUN; ++j) a[j] = __uint_as_float(ebits(rw, j, T{}) & 0x7FFFFFFFu);
+      part[i] = lane_tree<RUN>(a);
     }
-    float total = wave_tree<GPW>(part);
-    if (W > 1) {
-      if (lane == 0) red_sum[wid] = total;
-      __syncthreads();
-      total = tree16(&red_sum[row_in_block * W], W);
+    float total;
+    if constexpr (LPR == 64) {
+      total = wave_tree<GPW>(part);
+      if (W > 1) {
+        if (lane == 0) red_sum[wid] = total;
+        __syncthreads();
+        total = tree16(&red_sum[row_in_block * W], W);
+      }
+    } else {
+      total = lanes_tree<LPR>(part[0]);
     }
 
+    // Register pressure: make pass 2 convert the raw words again rather than
+    // keep pass 1's floats alive (an empty asm that claims to change them), and
+    // in RELOAD mode make it really re-read the runs (a compiler-only memory
+    // barrier keeps the second loads from being merged with the first ones).
+    if constexpr (RELOAD) {
+      __asm__ __volatile__("" ::: "memory");
+    } else {
+#pragma unroll
+      for (int i = 0; i < GPW; ++i)
+#pragma unroll
+        for (int w = 0; w < NW; ++w) __asm__ __volatile__("" : "+v"(raw[i][w]));
+    }
     uint32_t mbits[GPW], sbits[GPW];
     float alpha_v;
     int count = 0;
     if constexpr (TERNARY) {
       const float mu = total / fK;
       const float thr = 0.5f * mu;
-      // Pass 2: threshold, planes, tree(kept |x|), nnz.
+      const uint32_t uthr = __float_as_uint(thr);
+      // Pass 2: threshold, plane bytes, tree(kept |x|), nnz.
 #pragma unroll
       for (int i = 0; i < GPW; ++i) {
-        float kept[V];
+        if constexpr (RELOAD) fetch(i, raw[0]);
+        const uint32_t* rw = raw[RELOAD ? 0 : i];
+        float kept[RUN];
         uint32_t mb = 0, sb = 0;
 #pragma unroll
-        for (int j = 0; j < V; ++j) {
-          const float a = fabsf(x[i][j]);
-          const bool keep = a > thr;
-          kept[j] = keep ? a : 0.0f;
-          mb |= (uint32_t)keep << j;
-          sb |= (uint32_t)(keep && x[i][j] < 0.0f) << j;
+        for (int j = 0; j < RUN; ++j) {
+          const uint32_t ux = ebits(rw, j, T{});
+          const uint32_t ua = ux & 0x7FFFFFFFu;          // |x|
+          const uint32_t keep = gt_bit(ua, uthr);        // |x| > thr
+          kept[j] = __uint_as_float(ua & (0u - keep));   // keep ? |x| : +0
+          mb |= keep << j;
+          sb |= (keep & (ux >> 31)) << j;                // kept and negative
         }
-        part[i] = lane_tree<V>(kept);
+        part[i] = lane_tree<RUN>(kept);
         mbits[i] = mb;
         sbits[i] = sb;
         count += __builtin_popcount(mb);
       }
-      float ktot = wave_tree<GPW>(part);
-      int ctot = wave_sum_int(count);
-      if (W > 1) {
-        if (lane == 0) {
-          red_kept[wid] = ktot;
-          red_cnt[wid] = ctot;
+      float ktot;
+      int ctot;
+      if constexpr (LPR == 64) {
+        ktot = wave_tree<GPW>(part);
+        ctot = wave_sum_int(count);
+        if (W > 1) {
+          if (lane == 0) {
+            red_kept[wid] = ktot;
+            red_cnt[wid] = ctot;
+          }
+          __syncthreads();
+          ktot = tree16(&red_kept[row_in_block * W], W);
+          ctot = 0;
+          for (int q = 0; q < W; ++q) ctot += red_cnt[row_in_block * W + q];
         }
-        __syncthreads();
-        ktot = tree16(&red_kept[row_in_block * W], W);
-        ctot = 0;
-        for (int q = 0; q < W; ++q) ctot += red_cnt[row_in_block * W + q];
+      } else {
+        ktot = lanes_tree<LPR>(part[0]);
+        ctot = lanes_sum<LPR>(count);
       }
       count = ctot;
       alpha_v = ctot ? ktot / (float)ctot : 0.0f;
@@ -164,81 +267,185 @@ pack_rows_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t sr, i
       alpha_v = total / fK;
 #pragma unroll
       for (int i = 0; i < GPW; ++i) {
+        if constexpr (RELOAD) fetch(i, raw[0]);
+        const uint32_t* rw = raw[RELOAD ? 0 : i];
         uint32_t sb = 0;
 #pragma unroll
-        for (int j = 0; j < V; ++j) sb |= (uint32_t)(x[i][j] < 0.0f) << j;
+        for (int j = 0; j < RUN; ++j) sb |= neg_bit(ebits(rw, j, T{})) << j;
         sbits[i] = sb;
         mbits[i] = 0;
       }
     }
 
-    // Combine LPW lanes into one 32-bit word per plane and store it.
-    const int64_t base = (live ? r : 0) * row_bytes;
+    // Each lane stores its own byte of each plane (byte = (group*G + ll*8) / 8).
+    if (live) {
+      const int64_t base = r * row_bytes;
 #pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-      uint32_t m = mbits[i], s = sbits[i];
-#pragma unroll
-      for (int d = 1; d < LPW; d <<= 1) {
-        if constexpr (TERNARY) m |= (uint32_t)__shfl_down((int)m, d, kWave) << (d * V);
-        s |= (uint32_t)__shfl_down((int)s, d, kWave) << (d * V);
+      for (int i = 0; i < GPW; ++i) {
+        const int64_t byte = (int64_t)(w_in_row * GPW + i) * LPR + ll;
+        if (byte < row_bytes) {
+          if constexpr (TERNARY) mask[base + byte] = (uint8_t)mbits[i];
+          sign[base + byte] = (uint8_t)sbits[i];
+        }
       }
-      const int64_t bit = (int64_t)(w_in_row * GPW + i) * G + (int64_t)lane * V;
-      if (live && (lane % LPW) == 0 && bit < Kp) {
-        if constexpr (TERNARY) *reinterpret_cast<uint32_t*>(mask + base + bit / 8) = m;
-        *reinterpret_cast<uint32_t*>(sign + base + bit / 8) = s;
+      if (w_in_row == 0 && ll == 0) {
+        alpha[r] = alpha_v;
+        if constexpr (TERNARY) nnz[r] = count;
       }
     }
-    if (live && w_in_row == 0 && lane == 0) {
-      alpha[r] = alpha_v;
-      if constexpr (TERNARY) nnz[r] = count;
+  }
+}
+
+// Columns of a row-major [K, C] matrix with leading dimension ld: column c
+// becomes row c of the sign plane.  Block: W waves x 64 columns; wave w folds the
+// aligned range [w*P/W, (w+1)*P/W) of the zero-padded length P.
+constexpr int kStack = 14;  // runs per wave <= 2^13 (K <= 65536)
+
+template <typename T, int W>
+__global__ void __launch_bounds__(64 * W)
+pack_columns_kernel(const T* __restrict__ X, int64_t C, int64_t K, int64_t ld, int64_t P,
+                    int64_t row_bytes, uint8_t* __restrict__ sign, float* __restrict__ alpha) {
+  __shared__ float red[W][64];
+  const int lane = __lane_id();
+  const int wid = threadIdx.x / kWave;
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+  const bool live = c < C;
+  const int64_t span = P / W;
+  const int64_t k0 = (int64_t)wid * span;
+  const int64_t runs = (span + RUN - 1) / RUN;
+
+  float stack[kStack];
+#pragma unroll
+  for (int l = 0; l < kStack; ++l) stack[l] = 0.0f;
+  for (int64_t n = 0; n < runs; ++n) {
+    const int64_t kb = k0 + n * RUN;
+    float v[RUN];
+    uint32_t sb = 0;
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) {
+      const int64_t k = kb + j;
+      float x = 0.0f;
+      if (live && k < K && k < k0 + span) {
+        if constexpr (sizeof(T) == 4)
+          x = __uint_as_float(raw_bits(X[k * ld + c]));
+        else
+          x = bf16_bits_to_f32(raw_bits(X[k * ld + c]));
+      }
+      const uint32_t ux = __float_as_uint(x);
+      v[j] = __uint_as_float(ux & 0x7FFFFFFFu);
+      sb |= neg_bit(ux) << j;
     }
+    float node = lane_tree<RUN>(v);
+    // binary-counter merge: run n closes the levels of its trailing one bits
+    bool open = true;
+#pragma unroll
+    for (int l = 0; l < kStack; ++l) {
+      const bool merge = open && ((n >> l) & 1);
+      if (merge) node = stack[l] + node;
+      if (open && !merge) {
+        stack[l] = node;
+        open = false;
+      }
+    }
+    if (live && kb < K) sign[c * row_bytes + kb / 8] = (uint8_t)sb;
+  }
+  // Root of this wave's range: pending left nodes meet zero right siblings.
+  float root = 0.0f;
+#pragma unroll
+  for (int l = 0; l < kStack; ++l)
+    if ((runs >> l) & 1) root = stack[l] + root;
+  red[wid][lane] = root;
+  __syncthreads();
+  if (wid == 0 && live) {
+    float t[W];
+#pragma unroll
+    for (int q = 0; q < W; ++q) t[q] = red[q][lane];
+#pragma unroll
+    for (int w = W; w > 1; w >>= 1)
+#pragma unroll
+      for (int q = 0; q < w / 2; ++q) t[q] = t[2 * q] + t[2 * q + 1];
+    alpha[c] = t[0] / (float)K;
+    // zero the padding bytes of the row (k in [round_up(K, 8), Kp))
+    for (int64_t byte = (K + 7) / 8; byte < row_bytes; ++byte) sign[c * row_bytes + byte] = 0;
   }
 }
 
 struct Plan {
+  int lpr;    // lanes per row (16, 32 or 64)
   int gpw;    // groups per wave
   int W;      // waves per row
-  int wpb;    // waves per block
+  int block;  // threads per block
 };
 
-template <typename T>
 Plan plan_for(int64_t K) {
-  constexpr int G = kWave * Elem<T>::V;
-  int64_t n = (K + G - 1) / G;
-  int64_t p = 1;
-  while (p < n) p <<= 1;
   Plan pl;
-  pl.gpw = (int)(p < Elem<T>::GPW_MAX ? p : Elem<T>::GPW_MAX);
-  pl.W = (int)(p / pl.gpw);
-  pl.wpb = pl.W >= 4 ? pl.W : 4;
+  if (K <= 16 * RUN) {
+    pl = {16, 1, 1, 256};
+  } else if (K <= 32 * RUN) {
+    pl = {32, 1, 1, 256};
+  } else {
+    const int64_t n = (K + 64 * RUN - 1) / (64 * RUN);
+    int64_t p = 1;
+    while (p < n) p <<= 1;
+    pl.lpr = 64;
+    pl.gpw = (int)(p < 8 ? p : 8);
+    pl.W = (int)(p / pl.gpw);
+    pl.block = pl.W <= 4 ? 256 : 64 * pl.W;
+  }
   return pl;
 }
 
 template <typename T, bool TERNARY, bool VEC>
-hipError_t launch_typed(const T* X, int64_t rows, int64_t K, int64_t sr, int64_t sk, uint8_t* mask,
-                        uint8_t* sign, float* alpha, int32_t* nnz, hipStream_t stream) {
-  const Plan pl = plan_for<T>(K);
+hipError_t launch_rows(const T* X, int64_t rows, int64_t K, int64_t sr, int64_t sk, uint8_t* mask,
+                       uint8_t* sign, float* alpha, int32_t* nnz, hipStream_t stream) {
+  const Plan pl = plan_for(K);
   const int64_t row_bytes = (K + 63) / 64 * 8;
-  const int rpb = pl.wpb / pl.W;
+  const int wpb = pl.block / kWave;
+  const int rpb = pl.lpr == 64 ? wpb / pl.W : wpb * (kWave / pl.lpr);
   int64_t blocks = (rows + rpb - 1) / rpb;
   if (blocks > (1 << 20)) blocks = 1 << 20;
-  const dim3 grid((unsigned)blocks), block((unsigned)(pl.wpb * kWave));
-#define BWTA_PACK_CASE(G_)                                                                     \
-  case G_:                                                                                     \
-    if constexpr (G_ <= Elem<T>::GPW_MAX)                                                      \
-      hipLaunchKernelGGL((pack_rows_kernel<T, G_, TERNARY, VEC>), grid, block, 0, stream, X,   \
-                         rows, K, sr, sk, pl.W, row_bytes, mask, sign, alpha, nnz);            \
-    break;
-  switch (pl.gpw) {
-    BWTA_PACK_CASE(1)
-    BWTA_PACK_CASE(2)
-    BWTA_PACK_CASE(4)
-    BWTA_PACK_CASE(8)
-    BWTA_PACK_CASE(16)
-    default:
-      return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block((unsigned)pl.block);
+#define BWTA_ROWS(GPW_, LPR_, BLOCK_, RELOAD_)                                                  \
+  hipLaunchKernelGGL((pack_rows_kernel<T, GPW_, LPR_, TERNARY, VEC, BLOCK_, RELOAD_>), grid,      \
+                     block, 0, stream, X, rows, K, sr, sk, pl.W, row_bytes, mask, sign, alpha, nnz)
+  if (pl.lpr == 16) {
+    BWTA_ROWS(1, 16, 256, false);
+  } else if (pl.lpr == 32) {
+    BWTA_ROWS(1, 32, 256, false);
+  } else if (pl.block == 256) {
+    switch (pl.gpw) {
+      case 1: BWTA_ROWS(1, 64, 256, false); break;
+      case 2: BWTA_ROWS(2, 64, 256, false); break;
+      case 4: BWTA_ROWS(4, 64, 256, false); break;
+      default: BWTA_ROWS(8, 64, 256, false); break;
+    }
+  } else if (pl.block == 512) {
+    BWTA_ROWS(8, 64, 512, true);
+  } else {
+    BWTA_ROWS(8, 64, 1024, true);
   }
-#undef BWTA_PACK_CASE
+#undef BWTA_ROWS
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_columns(const T* X, int64_t C, int64_t K, int64_t ld, uint8_t* sign,
+                          float* alpha, hipStream_t stream) {
+  int64_t P = 1;
+  while (P < K) P <<= 1;
+  const int64_t row_bytes = (K + 63) / 64 * 8;
+  const dim3 grid((unsigned)((C + 63) / 64));
+  // W waves split the padded length P; each range must hold whole runs of 8.
+  if (P >= 16 * RUN) {
+    hipLaunchKernelGGL((pack_columns_kernel<T, 16>), grid, dim3(1024), 0, stream, X, C, K, ld, P,
+                       row_bytes, sign, alpha);
+  } else if (P >= 4 * RUN) {
+    hipLaunchKernelGGL((pack_columns_kernel<T, 4>), grid, dim3(256), 0, stream, X, C, K, ld, P,
+                       row_bytes, sign, alpha);
+  } else {
+    hipLaunchKernelGGL((pack_columns_kernel<T, 1>), grid, dim3(64), 0, stream, X, C, K, ld, P,
+                       row_bytes, sign, alpha);
+  }
   return hipGetLastError();
 }
 
@@ -246,16 +453,22 @@ template <bool TERNARY>
 hipError_t launch_any(const void* X, Elt dt, int64_t rows, int64_t K, int64_t sr, int64_t sk,
                       uint8_t* mask, uint8_t* sign, float* alpha, int32_t* nnz, hipStream_t stream) {
   const size_t es = dt == Elt::F32 ? 4 : 2;
-  const bool vec = sk == 1 && (reinterpret_cast<uintptr_t>(X) % 16 == 0) &&
+  if (!TERNARY && sk != 1 && sr == 1 && sk >= rows) {
+    return dt == Elt::F32
+               ? launch_columns<float>(static_cast<const float*>(X), rows, K, sk, sign, alpha, stream)
+               : launch_columns<uint16_t>(static_cast<const uint16_t*>(X), rows, K, sk, sign, alpha,
+                                          stream);
+  }
+  const bool vec = sk == 1 && K % RUN == 0 && (reinterpret_cast<uintptr_t>(X) % 16 == 0) &&
                    ((sr * (int64_t)es) % 16 == 0 || rows <= 1);
   if (dt == Elt::F32) {
     auto p = static_cast<const float*>(X);
-    return vec ? launch_typed<float, TERNARY, true>(p, rows, K, sr, sk, mask, sign, alpha, nnz, stream)
-               : launch_typed<float, TERNARY, false>(p, rows, K, sr, sk, mask, sign, alpha, nnz, stream);
+    return vec ? launch_rows<float, TERNARY, true>(p, rows, K, sr, sk, mask, sign, alpha, nnz, stream)
+               : launch_rows<float, TERNARY, false>(p, rows, K, sr, sk, mask, sign, alpha, nnz, stream);
   }
   auto p = static_cast<const uint16_t*>(X);
-  return vec ? launch_typed<uint16_t, TERNARY, true>(p, rows, K, sr, sk, mask, sign, alpha, nnz, stream)
-             : launch_typed<uint16_t, TERNARY, false>(p, rows, K, sr, sk, mask, sign, alpha, nnz, stream);
+  return vec ? launch_rows<uint16_t, TERNARY, true>(p, rows, K, sr, sk, mask, sign, alpha, nnz, stream)
+             : launch_rows<uint16_t, TERNARY, false>(p, rows, K, sr, sk, mask, sign, alpha, nnz, stream);
 }
 
 }  // namespace

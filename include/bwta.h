@@ -83,7 +83,8 @@ typedef enum { BWTA_F32 = 0, BWTA_BF16 = 1, BWTA_I32 = 2 } bwta_dtype;
  * bit planes to int8 {-1, 0, +1} and multiplies on the int8 matrix cores with
  * int32 accumulation; POPCOUNT evaluates
  *   acc = nnz - 2 * sum_words popcount((w & (mask ^ sign)) | (~w & sign))
- * on the vector ALUs. */
+ * on the vector ALUs.  Both give the same exact sums; for K <= 64 (one 64-bit
+ * word per row) MFMA requests run the popcount kernel. */
 typedef enum { BWTA_ALGO_AUTO = 0, BWTA_ALGO_MFMA = 1, BWTA_ALGO_POPCOUNT = 2 } bwta_algo;
 
 int bwta_version(void);

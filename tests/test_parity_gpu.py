@@ -118,6 +118,7 @@ def test_pack_weights_columns(bw, oracle, L, C, bf16):
 # products
 # ----------------------------------------------------------------------------
 GEMM_SHAPES = [(1, 1, 1), (5, 3, 64), (17, 33, 65), (128, 128, 256), (130, 260, 200),
+               (40, 50, 128), (33, 70, 192), (129, 257, 320), (70, 90, 448),
                (257, 129, 1000), (128, 768, 768), (300, 130, 4096), (64, 300, 11008),
                (200, 100, 28672 + 64)]
 
@@ -184,6 +185,17 @@ def test_batched_ternary_ternary(bw, oracle, H, L, D, algo):
     for h in range(H):
         ref = oracle.matmul_i32(tq[h * L:(h + 1) * L], tk[h * L:(h + 1) * L])
         assert (got[h] == ref).all(), f"head {h}"
+
+
+def test_pack_weights_columns_all_heads(bw, oracle):
+    """V laid out [L, H*D]: one call packs V^T of every head (row h*D + d)."""
+    rng = np.random.Generator(np.random.PCG64(3))
+    H, L, D = 5, 2048, 128
+    v = inputs.f32_to_bf16_bits(rng.standard_normal((L, H * D), dtype=np.float32))
+    got = bw.bwta_pack_weights(to_dev(v), transpose=True)
+    s, alpha = oracle.binarize(v, transpose=True)
+    assert (to_host(got.sign) == oracle.pack_plane(s, "sign")).all()
+    assert (to_host(got.alpha) == alpha).all()
 
 
 @pytest.mark.parametrize("algo", ["mfma", "popcount"])
