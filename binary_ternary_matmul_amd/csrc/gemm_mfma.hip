@@ -1,5 +1,7 @@
-// gemm_mfma.hip - binary x ternary and ternary x ternary products on the int8
-// matrix cores of gfx950 (v_mfma_i32_32x32x32_i8, int32 accumulation).
+// gemm_mfma.hip - binary x ternary and ternary x ternary products on the
+// matrix cores of gfx950, with {-1, 0, +1} operands encoded as FP4 (e2m1) and
+// multiplied by v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales, fp32
+// accumulation).
 //
 // BWTA page ("BWTA: Accurate and Efficient Binarized Transformer by
 // Algorithm-Hardware Co-design"), Abstract: a binary/ternary MatMul for the
@@ -7,26 +9,35 @@
 //   acc[m][n] = sum_k t[m][k] * s[n][k],   t in {-1,0,+1}, s in {-1,+1} (or t),
 // rescaled by alpha_a[m] * alpha_b[n] in the fused epilogue.
 //
+// Exactness: -1, 0 and +1 are exact e2m1 values, every product is -1, 0 or +1,
+// and every partial sum is an integer of magnitude <= K <= 65536 < 2^24, so
+// the fp32 accumulation is exact in any order and converts to the int32 sum
+// without rounding.
+//
 // Design (gfx950 first, not the page's CUDA kernel):
+// * FP4 is the narrowest operand the matrix cores take: a 32x32x64 FP4 MFMA
+//   does twice the k of the 32x32x32 int8 one in the same issue time, and a
+//   4-bit element is cheap to build from the bit planes.
 // * One wave owns a 128 x 128 output tile (4 x 4 MFMA tiles of 32 x 32, 256
-//   int32 accumulators per lane, held in AGPRs at one wave per SIMD; the
-//   32 x 32 form keeps the register allocator from splitting them).
-// * Operands stay packed until the last moment: the packed bit planes of each
-//   256-k step (32 bytes per row) are copied global -> LDS with direct 16-byte
-//   DMA loads, double-buffered per wave, and each lane expands the words it
-//   needs from LDS in registers directly into the MFMA operand layout.  The k
-//   order inside an MFMA is free as long as A and B use the same one: lane
-//   group g = lane/32 takes 64-bit words 2g and 2g+1 of the step, and dword d
-//   (0..7) of a 32-bit word holds in byte j the bit 8j + d.
-// * Expansion uses v_perm_b32 as a byte lookup (selector 0..7 picks a byte of
-//   the 8-byte table, 12 gives 0x00, >= 13 gives 0xFF, 8 copies the sign of
-//   byte 1):
-//     binary  : sel = w & (0x01010101 << d)         table {+1, -1, -1, ., -1}
-//     ternary : z  = (m & 0x0F0F0F0F) | ((s << 4) & 0xF0F0F0F0), and for the
-//               upper nibbles z' = ((m >> 4) & 0x0F0F0F0F) | (s & 0xF0F0F0F0);
-//               sel = z & (0x11111111 << i) for i = 0..2 and
-//               (z >> 1) & 0x44444444 for i = 3       table {0, +1, +1, ., +1}
-//   i.e. 2 VALU ops per 4 binary values and ~2.75 per 4 ternary values.
+//   fp32 accumulators per lane in AGPRs, one wave per SIMD).
+// * The packed planes of each 256-k step (32 bytes per row and plane) are
+//   copied global -> LDS with direct 16-byte DMA loads into a 3-deep ring per
+//   wave; lane (r, g) reads its 16 bytes of each row (32-bit words w0..w3 of
+//   half g) one step ahead and builds the MFMA operands in registers.
+// * k order: the order of k inside an MFMA is free as long as A and B agree
+//   (A nibble i of lane (r, g) meets B nibble i of lane (c, g)).  Slice e
+//   (0..3) of a step puts into nibble j of operand word x the bit 4j + e of
+//   source word wx.  Then an e2m1 nibble (bit 3 sign, bits 2..1 exponent,
+//   +1 = 0x2, -1 = 0xA) is a shift and a mask away:
+//     binary s  : ((w << (3 - e)) & 0x88888888) | 0x22222222
+//     ternary t : q01 = bfi(0x33333333, m, s << 2), q23 = bfi(0x33333333, m >> 2, s)
+//                 (mask and sign bits of k = 4j+e and 4j+e+1 side by side),
+//                 slice 0: (q01 << 1) & 0xAAAAAAAA, 1: q01 & 0xAAAAAAAA,
+//                 slice 2: (q23 << 1) & 0xAAAAAAAA, 3: q23 & 0xAAAAAAAA
+//   (a zero mask bit with a stray sign bit gives -0, which adds nothing).
+// * Software pipeline: the operands of slice e+1 are built while the 16 MFMAs
+//   of slice e run, and the next step's words are read, re-laid and built into
+//   slice 0 during slice 3, so the matrix cores never wait for a step boundary.
 // * K is split over S waves of one block (S in {1, 2, 4}) when the grid would
 //   otherwise leave SIMDs idle; the partial tiles are summed exactly in LDS.
 #include "device_common.hpp"
@@ -36,55 +47,20 @@ namespace bwta {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int TILES = 4;            // 32-row MFMA tiles per wave along M and along N
+constexpr int TILES = 4;  // 32-row MFMA tiles per wave along M and along N
 constexpr int WAVE_TILE = 32 * TILES;
+constexpr int kRing = 3;  // LDS stages per wave
+constexpr int kFmtFp4 = 4;       // cbsz / blgp format code of e2m1
+constexpr int kScaleOne = 127;   // E8M0 block scale 2^0
 
-// v_perm tables: __builtin_amdgcn_perm(hi, lo, sel) reads bytes 0..3 from lo
-// and 4..7 from hi.
-constexpr uint32_t kTernLo = 0x00010100u;  // byte0 = 0, bytes 1, 2 = +1
-constexpr uint32_t kTernHi = 0x00000001u;  // byte4 = +1
-constexpr uint32_t kBinLo = 0x00FFFF01u;   // byte0 = +1, bytes 1, 2 = -1
-constexpr uint32_t kBinHi = 0x000000FFu;   // byte4 = -1
-
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
-// Ternary operand for slice q (0: bits 8j+0..3, 1: bits 8j+4..7) of 32 k values.
-__device__ __forceinline__ v4i expand_ternary(uint32_t m, uint32_t s, int q) {
-  const uint32_t z = q == 0 ? ((m & 0x0F0F0F0Fu) | ((s << 4) & 0xF0F0F0F0u))
-                            : (((m >> 4) & 0x0F0F0F0Fu) | (s & 0xF0F0F0F0u));
-  v4i r;
-  r[0] = (int)perm(kTernHi, kTernLo, z & 0x11111111u);
-  r[1] = (int)perm(kTernHi, kTernLo, z & 0x22222222u);
-  r[2] = (int)perm(kTernHi, kTernLo, z & 0x44444444u);
-  r[3] = (int)perm(kTernHi, kTernLo, (z >> 1) & 0x44444444u);
-  return r;
-}
-
-// Binary (+-1) operand for the same slice.
-__device__ __forceinline__ v4i expand_binary(uint32_t w, int q) {
-  v4i r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (int)perm(kBinHi, kBinLo, w & (0x01010101u << (4 * q + i)));
-  return r;
-}
-
-__device__ __forceinline__ uint64_t ld64(const uint8_t* p) {
-  return *reinterpret_cast<const uint64_t*>(p);
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t x, uint32_t y) {
+  return (x & mask) | (y & ~mask);
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Packed words of one step held by a lane: words 2g and 2g+1 of the rows
-// 32t + r of each plane.
-template <bool B_TERNARY>
-struct Packed {
-  uint64_t am[TILES][2], as[TILES][2];
-  uint64_t bm[B_TERNARY ? TILES : 1][2], bs[TILES][2];
-};
 
 // LDS staging of one step (256 k = 32 bytes of each of 128 rows per plane).
 // Plane order in a stage: A mask, A sign, B sign, [B mask].
@@ -93,113 +69,134 @@ struct Stage {
   static constexpr int kPlane = WAVE_TILE * 32;
   static constexpr int kPlanes = B_TERNARY ? 4 : 3;
   static constexpr int kBytes = kPlane * kPlanes;
+  static constexpr int kLoads = 4 * kPlanes;  // DMA instructions per step and lane
 };
 
 // Copy 32 bytes (one 256-k step) of each of 128 rows of one plane into LDS
-// with direct global->LDS 16-byte loads: lane i of instruction j moves half
+// with direct buffer->LDS 16-byte loads: lane i of instruction j moves half
 // (i & 1) of row 32j + i/2, and the hardware stores lane i's 16 bytes at
-// dst + 16 i, so row rho lands at dst + 32 rho.  Every source stays inside the
-// matrix:
-// * rows past `valid` reuse the last valid row (their results are never stored);
-// * a half that starts past the row end reads the row start instead (its words
-//   are zeroed when the stage is read);
+// dst + 16 i, so row rho lands at dst + 32 rho.  Loads go through a raw buffer
+// descriptor of the tile's first row (base in SGPRs): the lane offset `off[j]`
+// is the VGPR offset, the step's byte offset `soff` the scalar one, so no
+// address arithmetic runs per load.  (Word 3 of the descriptor: 32-bit data
+// format, the value the gfx9 raw-buffer convention uses; no range check is
+// relied on, every offset stays inside the plane.)
+//
+// Lane offsets, computed once: off[j] = rho_j * row_bytes + (lane & 1) * 16 with
+// rho_j = min(32j + lane/2, valid - 1) (rows past `valid` reuse the last valid
+// row; their results are never stored).  The step that holds the row end
+// (row_bytes % 32 != 0) uses offsets that include its byte offset, with every
+// source kept inside the row:
+// * a half that starts past the row end reads the row start instead;
 // * a half that straddles the row end (row_bytes % 16 == 8) reads the 16 bytes
-//   that end at the row end, so the row's last word lands one word later in
-//   the stage than its position; read_stage compensates.  This needs
-//   row_bytes >= 16 (K > 64), which the launcher guarantees.
-// The address is a wave-uniform base plus a 32-bit lane offset.
-__device__ __forceinline__ void dma_plane(const uint8_t* __restrict__ plane, uint32_t row_bytes,
-                                          int valid, uint32_t st, uint8_t* dst, int lane) {
-  uint32_t o = st * 32 + (lane & 1) * 16;
-  if (o + 16 > row_bytes) o = o < row_bytes ? row_bytes - 16 : 0;
+//   that end at the row end, i.e. the row's last 64-bit word lands in the
+//   upper slot and the lower slot repeats the word before it.  B is staged the
+//   same way, so the pairs still meet.
+// Both kinds of stray A words are cleared in LDS before they are read
+// (clear_tail).  This needs row_bytes >= 16 (K > 64), which the launcher
+// guarantees.  A's 32-row blocks are also rotated by `rot` (LDS block t holds
+// the tile's rows 32 ((t + rot) % 4) ..), so that with split K the rows a wave
+// keeps are always its accumulators acc[0 .. 4/S).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base) {
+  // The base goes through readfirstlane: the descriptor must live in SGPRs, and
+  // the compiler does not always prove the tile origin wave-uniform.
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, 0x7FFFFFFF, 0x00020000);
+}
+
+__device__ __forceinline__ void dma_plane(__amdgpu_buffer_rsrc_t rsrc, const uint32_t (&off)[4],
+                                          uint32_t soff, uint8_t* dst) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int rho = min(32 * j + (lane >> 1), valid - 1);
-    __builtin_amdgcn_global_load_lds(plane + ((uint32_t)rho * row_bytes + o),
-                                     (lds_void_t*)(dst + j * 1024), 16, 0, 0);
-  }
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + j * 1024), 16, off[j], soff,
+                                             0, 0);
 }
 
-template <bool B_TERNARY>
-__device__ __forceinline__ void dma_step(const uint8_t* am, const uint8_t* as, const uint8_t* bm,
-                                         const uint8_t* bs, uint32_t row_bytes, int m_valid,
-                                         int n_valid, uint32_t st, uint8_t* stage, int lane) {
-  constexpr int P = Stage<B_TERNARY>::kPlane;
-  dma_plane(am, row_bytes, m_valid, st, stage, lane);
-  dma_plane(as, row_bytes, m_valid, st, stage + P, lane);
-  dma_plane(bs, row_bytes, n_valid, st, stage + 2 * P, lane);
-  if constexpr (B_TERNARY) dma_plane(bm, row_bytes, n_valid, st, stage + 3 * P, lane);
-}
+// s_waitcnt immediate for "vmcnt <= n" (expcnt and lgkmcnt at their no-wait
+// maxima); vmcnt is split over bits 3:0 and 15:14.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
-// Lane (r, g) reads 64-bit words 2g, 2g+1 of row 32t + r of each plane with one
-// 16-byte LDS read.  `shift`: the row's last word straddled the DMA window and
-// sits one slot late (it is word 2g, found in slot 2g+1).  Words past the row
-// end are zeroed on the A side, which zeroes their products whatever B holds.
-template <bool B_TERNARY>
-__device__ __forceinline__ void read_stage(Packed<B_TERNARY>& p, const uint8_t* stage, int r,
-                                           int g, bool shift, bool k0in, bool k1in) {
-  constexpr int P = Stage<B_TERNARY>::kPlane;
-  typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t Words[TILES][4];  // 32-bit words 4g..4g+3 of rows 32t + r
+
+// Lane (r, g) reads its 16 bytes of row 32t + r of one staged plane.
+__device__ __forceinline__ void read_words(Words& w, const uint8_t* plane, int r, int g) {
 #pragma unroll
   for (int t = 0; t < TILES; ++t) {
-    const int off = (32 * t + r) * 32 + 16 * g;
-    const u64x2 m = *reinterpret_cast<const u64x2*>(stage + off);
-    const u64x2 s = *reinterpret_cast<const u64x2*>(stage + P + off);
-    const u64x2 w = *reinterpret_cast<const u64x2*>(stage + 2 * P + off);
-    p.am[t][0] = k0in ? (shift ? m[1] : m[0]) : 0ull;
-    p.as[t][0] = k0in ? (shift ? s[1] : s[0]) : 0ull;
-    p.am[t][1] = k1in ? m[1] : 0ull;
-    p.as[t][1] = k1in ? s[1] : 0ull;
-    p.bs[t][0] = shift ? w[1] : w[0];
-    p.bs[t][1] = w[1];
-    if constexpr (B_TERNARY) {
-      const u64x2 bm = *reinterpret_cast<const u64x2*>(stage + 3 * P + off);
-      p.bm[t][0] = shift ? bm[1] : bm[0];
-      p.bm[t][1] = bm[1];
-    }
+    const u32x4 v = *reinterpret_cast<const u32x4*>(plane + (32 * t + r) * 32 + 16 * g);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) w[t][x] = v[x];
   }
 }
 
-// One 256-k step: 8 slices of 32 k per lane group (word w, 32-bit half h,
-// nibble half q).  Per slice the 4 B operands are expanded first, then each A
-// operand right before its 4 MFMAs.
-template <bool B_TERNARY>
-__device__ __forceinline__ void compute_step(const Packed<B_TERNARY>& p,
-                                             v16i (&acc)[TILES][TILES]) {
+// In the step that holds the row end, zero the A mask words of lane (r, g)
+// that lie past the row end or repeat the word before a straddling window, so
+// that they contribute nothing (a zero mask bit makes the A element +-0).
+// Each lane clears only the bytes it reads itself.
+__device__ __forceinline__ void clear_tail(uint8_t* stage, int r, int g, int st, int words,
+                                           bool straddle) {
+  const int kw = st * 4 + 2 * g;  // 64-bit word index of slot 0
+  const bool sh = straddle && kw == words - 1;
+  const bool keep0 = kw < words && !sh;
+  const bool keep1 = kw + 1 < words || sh;
 #pragma unroll
-  for (int w = 0; w < 2; ++w)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        v4i b[TILES];
-#pragma unroll
-        for (int t = 0; t < TILES; ++t) {
-          if constexpr (B_TERNARY)
-            b[t] = expand_ternary((uint32_t)(p.bm[t][w] >> (32 * h)),
-                                  (uint32_t)(p.bs[t][w] >> (32 * h)), q);
-          else
-            b[t] = expand_binary((uint32_t)(p.bs[t][w] >> (32 * h)), q);
-        }
-#pragma unroll
-        for (int i = 0; i < TILES; ++i) {
-          const v4i a = expand_ternary((uint32_t)(p.am[i][w] >> (32 * h)),
-                                       (uint32_t)(p.as[i][w] >> (32 * h)), q);
-#pragma unroll
-          for (int j = 0; j < TILES; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[j], acc[i][j], 0, 0, 0);
-        }
-      }
+  for (int t = 0; t < TILES; ++t) {
+    uint64_t* w = reinterpret_cast<uint64_t*>(stage + (32 * t + r) * 32 + 16 * g);
+    if (!keep0) w[0] = 0;
+    if (!keep1) w[1] = 0;
+  }
 }
 
-// Output tile in LDS: 128 rows of 128 int32, padded by 8 words per row so that
-// the accumulator writes (2 rows x 32 columns per instruction, 4 rows apart)
-// hit 64 distinct banks.
-constexpr int kTileLd = WAVE_TILE + 8;
-constexpr size_t kTileBytes = (size_t)WAVE_TILE * kTileLd * 4;
+// Ternary words with the (mask, sign) bits of k = 4j+e and 4j+e+1 side by
+// side: q01 for slices 0, 1 and q23 for slices 2, 3.
+__device__ __forceinline__ void prep_q01(const Words& m, const Words& s, Words& q) {
+#pragma unroll
+  for (int t = 0; t < TILES; ++t)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) q[t][x] = bfi(0x33333333u, m[t][x], s[t][x] << 2);
+}
+__device__ __forceinline__ void prep_q23(const Words& m, const Words& s, Words& q) {
+#pragma unroll
+  for (int t = 0; t < TILES; ++t)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) q[t][x] = bfi(0x33333333u, m[t][x] >> 2, s[t][x]);
+}
 
-template <bool B_TERNARY, int OUT>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// e2m1 operands of slice e: ternary from q01 (e = 0, 1) or q23 (e = 2, 3).
+__device__ __forceinline__ void ternary_slice(const Words& q, int e, v4i (&o)[TILES]) {
+#pragma unroll
+  for (int t = 0; t < TILES; ++t)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) o[t][x] = (int)((e & 1 ? q[t][x] : q[t][x] << 1) & 0xAAAAAAAAu);
+}
+
+// Binary operand of slice e: the sign bit moved to nibble bit 3 and merged with
+// the +1 pattern 0x22222222 by one v_bitop3_b32 (table 0xE2: S1 ? S0 : S2 with
+// the index S0*4 + S1*2 + S2).
+__device__ __forceinline__ void binary_slice(const Words& w, int e, v4i (&o)[TILES]) {
+#pragma unroll
+  for (int t = 0; t < TILES; ++t)
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      o[t][x] = (int)__builtin_amdgcn_bitop3_b32(w[t][x] << (3 - e), 0x88888888u, 0x22222222u,
+                                                 0xE2);
+}
+
+__device__ __forceinline__ v16f mfma_fp4(v4i a, v4i b, v16f c) {
+  const v8i a8 = __builtin_shufflevector(a, a, 0, 1, 2, 3, -1, -1, -1, -1);
+  const v8i b8 = __builtin_shufflevector(b, b, 0, 1, 2, 3, -1, -1, -1, -1);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, kFmtFp4, kFmtFp4, 0, kScaleOne,
+                                                          0, kScaleOne);
+}
+
+// LDS of the cross-wave reduction: every wave's partial sums of one owner's
+// rows, 64 KiB in all (within the rings whenever S > 1).
+constexpr size_t kXchgBytes = (size_t)TILES * TILES * 16 * kWave * 4;
+
+template <bool B_TERNARY, int OUT, int S>
+__global__ void __launch_bounds__(S * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__ a_sign,
                  const float* __restrict__ a_alpha, int64_t a_batch_rows,
                  const uint8_t* __restrict__ b_mask, const uint8_t* __restrict__ b_sign,
@@ -207,9 +204,8 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
                  int64_t row_bytes, int tiles_m, int tiles_n, void* __restrict__ Y, int64_t ldy,
                  int64_t y_batch_stride) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int S = blockDim.x / kWave;
   const int lane = __lane_id();
-  const int wid = threadIdx.x / kWave;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int r = lane & 31;
   const int g = lane >> 5;
 
@@ -238,143 +234,361 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   const int64_t steps = (words + 3) / 4;        // 4 words (256 k) per step
   const int64_t st0 = steps * wid / S;
   const int64_t st1 = steps * (wid + 1) / S;
+  constexpr int TPW = TILES / S;  // 32-row blocks of the tile each wave finally owns
+  const int rot = wid * TPW;      // acc[t] accumulates the tile's row block (t + rot) % 4
 
-  // The tile's scales go to LDS now; the loads complete behind the main loop
-  // and the epilogue reads them from LDS (made visible by its first barrier).
+  // The tile's scales: wave 0 loads them first thing, the first DMAs go out
+  // behind them, and the wait for the first step (which completes them too)
+  // precedes their store to LDS, so their latency hides under the DMA's.
   __shared__ float s_alpha_a[WAVE_TILE], s_alpha_b[WAVE_TILE];
-  if constexpr (OUT != (int)Elt::I32) {
-    if (wid == 0) {
+  float ra[WAVE_TILE / kWave], rbv[WAVE_TILE / kWave];
+  const bool scale_wave = OUT != (int)Elt::I32 && wid == 0;
+  if (scale_wave) {
 #pragma unroll
-      for (int h = 0; h < WAVE_TILE / kWave; ++h) {
-        const int i = h * kWave + lane;
-        s_alpha_a[i] = i < m_valid ? a_alpha[b * a_batch_rows + m0 + i] : 0.0f;
-        s_alpha_b[i] = i < n_valid ? b_alpha[b * b_batch_rows + n0 + i] : 0.0f;
-      }
+    for (int h = 0; h < WAVE_TILE / kWave; ++h) {
+      const int i = h * kWave + lane;
+      ra[h] = i < m_valid ? a_alpha[b * a_batch_rows + m0 + i] : 0.0f;
+      rbv[h] = i < n_valid ? b_alpha[b * b_batch_rows + n0 + i] : 0.0f;
     }
   }
-
-  v16i acc[TILES][TILES];
+  auto store_scales = [&]() {
+    if (scale_wave) {
+#pragma unroll
+      for (int h = 0; h < WAVE_TILE / kWave; ++h) {
+        s_alpha_a[h * kWave + lane] = ra[h];
+        s_alpha_b[h * kWave + lane] = rbv[h];
+      }
+    }
+  };
+  v16f acc[TILES][TILES];
 #pragma unroll
   for (int i = 0; i < TILES; ++i)
 #pragma unroll
     for (int j = 0; j < TILES; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0;
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // Double-buffered LDS stages of this wave: step st+1 is in flight while step
-  // st is expanded and multiplied.
-  uint8_t* stages = smem + (size_t)wid * 2 * Stage<B_TERNARY>::kBytes;
+  constexpr int SB = Stage<B_TERNARY>::kBytes;
+  constexpr int P = Stage<B_TERNARY>::kPlane;
+  constexpr int L = Stage<B_TERNARY>::kLoads;
+  uint8_t* ring = smem + (size_t)wid * kRing * SB;
   const uint32_t rb = (uint32_t)row_bytes;
-  const bool straddle = (rb & 15u) == 8u;  // the last word is read one slot late
-  if (st0 < st1) dma_step<B_TERNARY>(am, as, bm, bs, rb, m_valid, n_valid, (uint32_t)st0, stages, lane);
-  for (int64_t st = st0; st < st1; ++st) {
-    uint8_t* stage = stages + ((st - st0) & 1) * Stage<B_TERNARY>::kBytes;
-    Packed<B_TERNARY> p;
-    // vmcnt(0) (expcnt/lgkmcnt fields at their no-wait maxima): the DMA of this
-    // step has landed in LDS.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    if (st * 4 + 4 <= words) {
-      read_stage<B_TERNARY>(p, stage, r, g, false, true, true);
-    } else {  // the row ends inside this step
-      const int64_t kw = st * 4 + 2 * g;
-      read_stage<B_TERNARY>(p, stage, r, g, straddle && kw == words - 1, kw < words,
-                            kw + 1 < words);
+  const bool straddle = (rb & 15u) == 8u;
+  if (st0 < st1) {
+    const int w32 = (int)words, s0i = (int)st0, s1i = (int)st1, last = s1i - 1;
+    // DMA lane offsets: full-step form (offa/offb, plus the step's byte offset
+    // as the scalar offset) until the step that holds the row end, whose own
+    // offsets (offa_t/offb_t) replace them from then on.
+    const int tail_st = (rb & 31u) ? (int)steps - 1 : 0x7FFFFFFF;
+    uint32_t offa[4], offb[4], offa_t[4], offb_t[4];
+    {
+      const uint32_t half = (lane & 1) * 16;
+      uint32_t ot = (uint32_t)(steps - 1) * 32 + half;
+      if (ot + 16 > rb) ot = ot < rb ? rb - 16 : 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t ra_ = (uint32_t)min(32 * ((j + rot) & 3) + (lane >> 1), m_valid - 1) * rb;
+        const uint32_t rb_ = (uint32_t)min(32 * j + (lane >> 1), n_valid - 1) * rb;
+        offa[j] = ra_ + half;
+        offb[j] = rb_ + half;
+        offa_t[j] = ra_ + ot;
+        offb_t[j] = rb_ + ot;
+      }
     }
-    if (st + 1 < st1)
-      dma_step<B_TERNARY>(am, as, bm, bs, rb, m_valid, n_valid, (uint32_t)(st + 1),
-                          stages + ((st + 1 - st0) & 1) * Stage<B_TERNARY>::kBytes, lane);
-    compute_step<B_TERNARY>(p, acc);
+    // Descriptors stay plain locals (inside an aggregate they can land in VGPRs).
+    const __amdgpu_buffer_rsrc_t ram = uniform_rsrc(am), ras = uniform_rsrc(as), rbs = uniform_rsrc(bs);
+    const __amdgpu_buffer_rsrc_t rbm = B_TERNARY ? uniform_rsrc(bm) : rbs;
+    // Ring of 3 slots: step s0i + i lives in slot i % 3.  Steps past the wave's
+    // range reload its last step (never used), which keeps the wait counts
+    // uniform.  step_soff() picks the step (clamped) and returns its scalar
+    // offset, switching to the row-end offsets when it gets there.
+    auto step_soff = [&](int st) -> uint32_t {
+      const int sd = min(st, last);
+      if (sd == tail_st) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          offa[j] = offa_t[j];
+          offb[j] = offb_t[j];
+        }
+        return 0u;
+      }
+      return (uint32_t)sd * 32;
+    };
+    auto dma = [&](int st, uint8_t* slot) {  // all planes of one step
+      const uint32_t so = step_soff(st);
+      dma_plane(ram, offa, so, slot);
+      dma_plane(ras, offa, so, slot + P);
+      dma_plane(rbs, offb, so, slot + 2 * P);
+      if constexpr (B_TERNARY) dma_plane(rbm, offb, so, slot + 3 * P);
+    };
+    uint8_t* slot0 = ring;           // step st
+    uint8_t* slot1 = ring + SB;      // step st + 1
+    uint8_t* slot2 = ring + 2 * SB;  // step st + 2
+
+    // Registers, for the step st being multiplied:
+    //   qa01/qa23 (and qb01/qb23): its prepared ternary words;  wb: its binary
+    //   B words;  na_m/na_s (nb_m/nb_s): raw words of a later step;
+    //   oa/ob: operands of the slice in flight and of the next one.
+    Words qa01, qa23, qb01, qb23, wb, na_m, na_s, nb_m, nb_s;
+    v4i oa[2][TILES], ob[2][TILES];
+
+    auto ready = [&](int st, uint8_t* slot) {  // stray A words of the row-end step
+      if (st * 32 + 32 > (int)rb) clear_tail(slot, r, g, st, w32, straddle);
+    };
+    dma(s0i, slot0);
+    dma(s0i + 1, slot1);
+    dma(s0i + 2, slot2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * L));  // step st0 (and the scales) landed
+    store_scales();
+    ready(s0i, slot0);
+    read_words(na_m, slot0, r, g);
+    read_words(na_s, slot0 + P, r, g);
+    if constexpr (B_TERNARY) {
+      read_words(nb_s, slot0 + 2 * P, r, g);
+      read_words(nb_m, slot0 + 3 * P, r, g);
+      prep_q01(nb_m, nb_s, qb01);
+      prep_q23(nb_m, nb_s, qb23);
+      ternary_slice(qb01, 0, ob[0]);
+    } else {
+      read_words(wb, slot0 + 2 * P, r, g);
+      binary_slice(wb, 0, ob[0]);
+    }
+    prep_q01(na_m, na_s, qa01);
+    prep_q23(na_m, na_s, qa23);
+    ternary_slice(qa01, 0, oa[0]);
+
+#define BWTA_MFMA_SLICE(C)                                                              \
+  _Pragma("unroll") for (int i = 0; i < TILES; ++i)                                    \
+  _Pragma("unroll") for (int j = 0; j < TILES; ++j)                                    \
+      acc[i][j] = mfma_fp4(ob[C][j], oa[C][i], acc[i][j])
+#define BWTA_REGION_END()                                                               \
+  do {                                                                                  \
+    _Pragma("unroll") for (int k = 0; k < TILES * TILES; ++k) {                         \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* 1 MFMA */                   \
+      if (k % 4 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); /* 1 DMA */    \
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0); /* up to 6 VALU */             \
+    }                                                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+  } while (0)
+
+    // Per step st: at the top, wait for step st + 1 (st + 2 may still be in
+    // flight), clear its stray words if it holds the row end, and start reading
+    // step st + 1's A words.  Then four regions, one per slice, each running its
+    // 16 MFMAs with the VALU work below spread between them, and each refilling
+    // one plane of the slot of step st (all in registers by now) with step
+    // st + 3:
+    //   A: build slice 1;  prepare q01 of step st + 1 (q01 of st is done)
+    //   B: build slice 2
+    //   C: build slice 3;  re-read step st + 1's A words, prepare its q23;
+    //      read its binary B words
+    //   D: build slice 0 of step st + 1
+    for (int st = s0i; st < s1i; ++st) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
+      ready(st + 1, slot1);
+      const uint32_t so = step_soff(st + 3);
+      read_words(na_m, slot1, r, g);
+      read_words(na_s, slot1 + P, r, g);
+      if constexpr (B_TERNARY) {
+        read_words(nb_s, slot1 + 2 * P, r, g);
+        read_words(nb_m, slot1 + 3 * P, r, g);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // A
+      ternary_slice(qa01, 1, oa[1]);
+      if constexpr (B_TERNARY)
+        ternary_slice(qb01, 1, ob[1]);
+      else
+        binary_slice(wb, 1, ob[1]);
+      prep_q01(na_m, na_s, qa01);
+      if constexpr (B_TERNARY) prep_q01(nb_m, nb_s, qb01);
+      dma_plane(ram, offa, so, slot0);  // step st + 3 into the slot of step st
+      BWTA_MFMA_SLICE(0);
+      BWTA_REGION_END();
+      // B
+      ternary_slice(qa23, 2, oa[0]);
+      if constexpr (B_TERNARY)
+        ternary_slice(qb23, 2, ob[0]);
+      else
+        binary_slice(wb, 2, ob[0]);
+      dma_plane(ras, offa, so, slot0 + P);
+      BWTA_MFMA_SLICE(1);
+      BWTA_REGION_END();
+      // C
+      read_words(na_m, slot1, r, g);
+      read_words(na_s, slot1 + P, r, g);
+      if constexpr (B_TERNARY) {
+        read_words(nb_s, slot1 + 2 * P, r, g);
+        read_words(nb_m, slot1 + 3 * P, r, g);
+      }
+      ternary_slice(qa23, 3, oa[1]);
+      if constexpr (B_TERNARY)
+        ternary_slice(qb23, 3, ob[1]);
+      else
+        binary_slice(wb, 3, ob[1]);
+      prep_q23(na_m, na_s, qa23);
+      if constexpr (B_TERNARY)
+        prep_q23(nb_m, nb_s, qb23);
+      else
+        read_words(wb, slot1 + 2 * P, r, g);
+      dma_plane(rbs, offb, so, slot0 + 2 * P);
+      BWTA_MFMA_SLICE(0);
+      BWTA_REGION_END();
+      // D
+      ternary_slice(qa01, 0, oa[0]);
+      if constexpr (B_TERNARY)
+        ternary_slice(qb01, 0, ob[0]);
+      else
+        binary_slice(wb, 0, ob[0]);
+      if constexpr (B_TERNARY) dma_plane(rbm, offb, so, slot0 + 3 * P);
+      BWTA_MFMA_SLICE(1);
+      BWTA_REGION_END();
+      uint8_t* const done = slot0;
+      slot0 = slot1;
+      slot1 = slot2;
+      slot2 = done;
+    }
+#undef BWTA_MFMA_SLICE
+#undef BWTA_REGION_END
+  } else {
+    store_scales();
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA may land in LDS from here on
+
+  // Accumulator layout: acc[t][j] = B_j x A_i^T with i = (t + rot) % 4, i.e. the
+  // MFMA's rows run over the output columns.  Register q of lane (r, g) holds
+  // output element
+  //   row 32i + r,  column 32j + 8 (q / 4) + 4g + q % 4,
+  // so each lane owns runs of 4 consecutive columns.  The fp32 sums are exact
+  // integers.
+  //
+  // Cross-wave reduction (S > 1): wave w owns the row blocks it holds in
+  // acc[0 .. TPW) (blocks rot .. rot + TPW - 1) and, in round k, hands
+  // acc[k TPW .. (k+1) TPW) - the blocks of wave (w + k) % S - to that wave
+  // through LDS, in a lane-major layout (each lane moves its own registers, 16
+  // bytes at a time), while adding wave (w - k) % S's share of its own blocks.
+  // fp32 adds of integers below 2^24 are exact.
+  if constexpr (S > 1) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    v4f* xbuf = reinterpret_cast<v4f*>(smem);
+    constexpr int region = TPW * TILES * 4 * kWave;  // float4s per wave
+    __syncthreads();  // every wave is done with its ring
+#pragma unroll
+    for (int k = 1; k < S; ++k) {
+      const int from = (wid - k) & (S - 1);
+#pragma unroll
+      for (int ii = 0; ii < TPW; ++ii)
+#pragma unroll
+        for (int j = 0; j < TILES; ++j) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const v16f& a = acc[k * TPW + ii][j];
+            const v4f v = {a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]};
+            xbuf[wid * region + ((ii * TILES + j) * 4 + c) * kWave + lane] = v;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      __syncthreads();
+#pragma unroll
+      for (int ii = 0; ii < TPW; ++ii)
+#pragma unroll
+        for (int j = 0; j < TILES; ++j) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const v4f v = xbuf[from * region + ((ii * TILES + j) * 4 + c) * kWave + lane];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[ii][j][4 * c + u] += v[u];
+          }
+          __builtin_amdgcn_sched_barrier(0);  // one 32x32 tile at a time: few live VGPRs
+        }
+      __syncthreads();
+    }
   }
 
-  // Sum the S partial tiles exactly in one LDS tile (wave 0 stores, the others
-  // add with LDS integer atomics), then let all S waves write the result.
-  // D[i][j] of a 32x32 MFMA tile sits in lane j + 32*((i/4)%2), register
-  // (i%4) + 4*(i/8).
-  int32_t* tile = reinterpret_cast<int32_t*>(smem);
-  __syncthreads();  // every wave is done with its stages
-  if (wid == 0) {
+  // Epilogue straight from the registers of the owned tile rows: y = acc *
+  // (alpha_a[row] * alpha_b[col]) in fp32 (the product of the scales first),
+  // bf16 rounded to nearest even (v_cvt_pk_bf16_f32), or the int32 sum itself.
+  // Each store writes a lane's 4 consecutive columns (8 or 16 bytes).  Complete
+  // tiles store through a buffer descriptor of the tile origin: the lane's
+  // offset in a VGPR, the tile row in an SGPR, the column block as an
+  // immediate.  Edge tiles check every element.
+  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  constexpr int ES = OUT == (int)Elt::BF16 ? 2 : 4;
+  char* ytile = static_cast<char*>(Y) + (b * y_batch_stride + m0 * ldy + n0) * ES;
+  // The column scales of this lane's 64 columns, read once.
+  float ab[TILES][4][4];
 #pragma unroll
-    for (int i = 0; i < TILES; ++i)
+  for (int j = 0; j < TILES; ++j)
+#pragma unroll
+    for (int qh = 0; qh < 4; ++qh) {
+      float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if constexpr (OUT != (int)Elt::I32)
+        v = *reinterpret_cast<const float4*>(&s_alpha_b[32 * j + 8 * qh + 4 * g]);
+      ab[j][qh][0] = v.x;
+      ab[j][qh][1] = v.y;
+      ab[j][qh][2] = v.z;
+      ab[j][qh][3] = v.w;
+    }
+  const bool full = m_valid == WAVE_TILE && n_valid == WAVE_TILE &&
+                    (int64_t)WAVE_TILE * ldy * ES < (int64_t)0x7FFFFFFF;
+  const __amdgpu_buffer_rsrc_t yrs = uniform_rsrc(ytile);
+  const uint32_t ldb = (uint32_t)(ldy * ES);
+  const uint32_t lane_off = r * ldb + 4 * g * ES;
+  // Per owned row block: every accumulator is read once into the output words
+  // (4 consecutive columns per (j, qh)), then stored - wide when the tile is
+  // complete, element by element with bounds checks otherwise.
+#pragma unroll
+  for (int ii = 0; ii < TPW; ++ii) {
+    const int i = (ii + rot) & 3;  // tile row block of acc[ii]
+    const int row = 32 * i + r;
+    const float aa = OUT != (int)Elt::I32 ? s_alpha_a[row] : 0.0f;
+    uint32_t o[TILES][4][4];
+#pragma unroll
+    for (int j = 0; j < TILES; ++j)
+#pragma unroll
+      for (int qh = 0; qh < 4; ++qh)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float a = acc[ii][j][4 * qh + u];
+          if constexpr (OUT == (int)Elt::I32)
+            o[j][qh][u] = (uint32_t)(int)a;
+          else if constexpr (OUT == (int)Elt::F32)
+            o[j][qh][u] = __float_as_uint(a * (aa * ab[j][qh][u]));
+          else
+            o[j][qh][u] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(a * (aa * ab[j][qh][u])));
+        }
+    if (full) {
+      const int soff = (int)__builtin_amdgcn_readfirstlane(32 * i * ldb);
 #pragma unroll
       for (int j = 0; j < TILES; ++j)
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          tile[(32 * i + (q & 3) + 8 * (q >> 2) + 4 * g) * kTileLd + 32 * j + r] = acc[i][j][q];
-  }
-  if (S > 1) {
-    __syncthreads();
-    if (wid != 0) {
-#pragma unroll
-      for (int i = 0; i < TILES; ++i)
-#pragma unroll
-        for (int j = 0; j < TILES; ++j)
-#pragma unroll
-          for (int q = 0; q < 16; ++q)
-            atomicAdd(&tile[(32 * i + (q & 3) + 8 * (q >> 2) + 4 * g) * kTileLd + 32 * j + r],
-                      acc[i][j][q]);
-    }
-  }
-  __syncthreads();
-
-  // Epilogue: each wave takes rows wid, wid + S, ...; a half-wave covers one
-  // 128-column row with 4 columns per lane, so every store is row-contiguous
-  // (one 16- or 8-byte store per lane when the row is aligned and complete).
-  const int half = lane >> 5;
-  const int c4 = (lane & 31) * 4;
-  float ab[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if constexpr (OUT != (int)Elt::I32) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) ab[u] = s_alpha_b[c4 + u];
-  }
-  constexpr int ES = OUT == (int)Elt::BF16 ? 2 : 4;
-  const bool vec_ok = ((ldy * ES) % 16 == 0) && ((y_batch_stride * ES) % 16 == 0) &&
-                      ((n0 * ES) % 16 == 0) && (reinterpret_cast<uintptr_t>(Y) % 16 == 0);
-  const bool full_cols = c4 + 4 <= n_valid;
-  char* ybase = static_cast<char*>(Y);
-  for (int row = 2 * wid + half; row < m_valid; row += 2 * S) {
-    const int4 v = *reinterpret_cast<const int4*>(&tile[row * kTileLd + c4]);
-    const int vv[4] = {v.x, v.y, v.z, v.w};
-    const int64_t yoff = b * y_batch_stride + (m0 + row) * ldy + n0 + c4;
-    if constexpr (OUT == (int)Elt::I32) {
-      int32_t* y = reinterpret_cast<int32_t*>(ybase) + yoff;
-      if (vec_ok && full_cols) {
-        *reinterpret_cast<int4*>(y) = v;
-      } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (c4 + u < n_valid) y[u] = vv[u];
-      }
-    } else {
-      const float aa = s_alpha_a[row];
-      float out[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float sc = aa * ab[u];
-        out[u] = (float)vv[u] * sc;
-      }
-      if constexpr (OUT == (int)Elt::F32) {
-        float* y = reinterpret_cast<float*>(ybase) + yoff;
-        if (vec_ok && full_cols) {
-          *reinterpret_cast<float4*>(y) = make_float4(out[0], out[1], out[2], out[3]);
-        } else {
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (c4 + u < n_valid) y[u] = out[u];
+        for (int qh = 0; qh < 4; ++qh) {
+          const int voff = (int)(lane_off + (32 * j + 8 * qh) * ES);
+          const uint32_t(&w)[4] = o[j][qh];
+          if constexpr (ES == 4) {
+            const v4u d = {w[0], w[1], w[2], w[3]};
+            __builtin_amdgcn_raw_buffer_store_b128(d, yrs, voff, soff, 0);
+          } else {
+            const v2u d = {w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+            __builtin_amdgcn_raw_buffer_store_b64(d, yrs, voff, soff, 0);
+          }
         }
-      } else {
-        uint16_t* y = reinterpret_cast<uint16_t*>(ybase) + yoff;
-        uint16_t h[4];
+    } else if (row < m_valid) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) h[u] = f32_to_bf16_rne(out[u]);
-        if (vec_ok && full_cols) {
-          *reinterpret_cast<uint2*>(y) = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),
-                                                    (uint32_t)h[2] | ((uint32_t)h[3] << 16));
-        } else {
+      for (int j = 0; j < TILES; ++j)
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (c4 + u < n_valid) y[u] = h[u];
-        }
-      }
+        for (int qh = 0; qh < 4; ++qh)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int col = 32 * j + 8 * qh + 4 * g + u;
+            if (col < n_valid) {
+              char* yp = ytile + ((int64_t)row * ldy + col) * ES;
+              if constexpr (ES == 4)
+                *reinterpret_cast<uint32_t*>(yp) = o[j][qh][u];
+              else
+                *reinterpret_cast<uint16_t*>(yp) = (uint16_t)o[j][qh][u];
+            }
+          }
     }
   }
 }
@@ -397,6 +611,35 @@ int choose_split(int64_t tiles, int64_t steps) {
   return best;
 }
 
+template <bool B_TERNARY, int OUT, int S>
+hipError_t launch_k(const GemmArgs& g, int64_t row_bytes, int64_t tm, int64_t tn,
+                    hipStream_t stream) {
+  size_t lds = (size_t)S * kRing * Stage<B_TERNARY>::kBytes;
+  if (S > 1 && lds < kXchgBytes) lds = kXchgBytes;
+  auto kfn = gemm_mfma_kernel<B_TERNARY, OUT, S>;
+  hipError_t e =
+      hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kfn, dim3((unsigned)(tm * tn), 1, (unsigned)g.batch), dim3(S * kWave), lds,
+                     stream, g.a_mask, g.a_sign, g.a_alpha, g.a_batch_rows, g.b_mask, g.b_sign,
+                     g.b_alpha, g.b_batch_rows, g.M, g.N, row_bytes, (int)tm, (int)tn, g.Y, g.ldy,
+                     g.y_batch_stride);
+  return hipGetLastError();
+}
+
+template <bool B_TERNARY, int OUT>
+hipError_t launch_s(const GemmArgs& g, int S, int64_t row_bytes, int64_t tm, int64_t tn,
+                    hipStream_t stream) {
+  switch (S) {
+    case 1:
+      return launch_k<B_TERNARY, OUT, 1>(g, row_bytes, tm, tn, stream);
+    case 2:
+      return launch_k<B_TERNARY, OUT, 2>(g, row_bytes, tm, tn, stream);
+    default:
+      return launch_k<B_TERNARY, OUT, 4>(g, row_bytes, tm, tn, stream);
+  }
+}
+
 template <bool B_TERNARY>
 hipError_t launch_b(const GemmArgs& g, hipStream_t stream) {
   const int64_t row_bytes = (g.K + 63) / 64 * 8;
@@ -404,33 +647,14 @@ hipError_t launch_b(const GemmArgs& g, hipStream_t stream) {
   const int64_t tn = (g.N + WAVE_TILE - 1) / WAVE_TILE;
   const int64_t steps = (row_bytes / 8 + 3) / 4;
   const int S = choose_split(tm * tn * g.batch, steps);
-  const dim3 grid((unsigned)(tm * tn), 1, (unsigned)g.batch);
-  const dim3 block((unsigned)(S * kWave));
-  size_t lds = (size_t)S * 2 * Stage<B_TERNARY>::kBytes;
-  if (lds < kTileBytes) lds = kTileBytes;
-#define BWTA_GEMM_LAUNCH(OUT_)                                                                  \
-  do {                                                                                          \
-    auto kfn = gemm_mfma_kernel<B_TERNARY, OUT_>;                                               \
-    hipError_t e = hipFuncSetAttribute((const void*)kfn,                                        \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);   \
-    if (e != hipSuccess) return e;                                                              \
-    hipLaunchKernelGGL(kfn, grid, block, lds, stream, g.a_mask, g.a_sign, g.a_alpha,            \
-                       g.a_batch_rows, g.b_mask, g.b_sign, g.b_alpha, g.b_batch_rows, g.M, g.N, \
-                       row_bytes, (int)tm, (int)tn, g.Y, g.ldy, g.y_batch_stride);                       \
-  } while (0)
   switch (g.y_dt) {
     case Elt::F32:
-      BWTA_GEMM_LAUNCH((int)Elt::F32);
-      break;
+      return launch_s<B_TERNARY, (int)Elt::F32>(g, S, row_bytes, tm, tn, stream);
     case Elt::BF16:
-      BWTA_GEMM_LAUNCH((int)Elt::BF16);
-      break;
-    case Elt::I32:
-      BWTA_GEMM_LAUNCH((int)Elt::I32);
-      break;
+      return launch_s<B_TERNARY, (int)Elt::BF16>(g, S, row_bytes, tm, tn, stream);
+    default:
+      return launch_s<B_TERNARY, (int)Elt::I32>(g, S, row_bytes, tm, tn, stream);
   }
-#undef BWTA_GEMM_LAUNCH
-  return hipGetLastError();
 }
 
 }  // namespace
