@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libbwta.so")
 
 BWTA_OK, BWTA_ERR_INVALID, BWTA_ERR_ALIGN, BWTA_ERR_UNSUPPORTED, BWTA_ERR_HIP = range(5)
 DTYPES = {"f32": 0, "bf16": 1, "i32": 2}
-ALGOS = {"auto": 0, "mfma": 1, "popcount": 2}
+ALGOS = {"auto": 0, "mfma": 1, "popcount": 2, "mfma_i8": 3}
 _TORCH_DT = {torch.float32: 0, torch.bfloat16: 1, torch.int32: 2}
 _OUT_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}
 

@@ -67,7 +67,8 @@ bwta_status check_product(const uint8_t* a_mask, const uint8_t* a_sign, const fl
   if (M < 0 || N < 0) return fail(BWTA_ERR_INVALID, "negative size M=%lld N=%lld", (long long)M, (long long)N);
   BWTA_TRY(check_k(K));
   if (!valid_out_dtype(y_dtype)) return fail(BWTA_ERR_INVALID, "bad output dtype %d", (int)y_dtype);
-  if (algo != BWTA_ALGO_AUTO && algo != BWTA_ALGO_MFMA && algo != BWTA_ALGO_POPCOUNT)
+  if (algo != BWTA_ALGO_AUTO && algo != BWTA_ALGO_MFMA && algo != BWTA_ALGO_POPCOUNT &&
+      algo != BWTA_ALGO_MFMA_I8)
     return fail(BWTA_ERR_INVALID, "bad algo %d", (int)algo);
   if (ldy < N) return fail(BWTA_ERR_INVALID, "ldy (%lld) < N (%lld)", (long long)ldy, (long long)N);
   if (M == 0 || N == 0) return BWTA_OK;  // empty: pointers may be NULL
@@ -165,6 +166,8 @@ static bwta_status run_product(const bwta::GemmArgs& g, bwta_algo algo, bool gem
     // One 64-bit word per row: below the MFMA kernel's 16-byte DMA window;
     // the popcount kernel computes the same exact sums.
     e = bwta::launch_gemm_popcount(g, stream);
+  } else if (algo == BWTA_ALGO_MFMA_I8) {
+    e = bwta::launch_gemm_mfma_i8(g, stream);
   } else {
     e = bwta::launch_gemm_mfma(g, stream);
   }

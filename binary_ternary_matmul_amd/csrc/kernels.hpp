@@ -37,6 +37,7 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_gemm_mfma_i8(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemm_popcount(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemv_popcount(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemv_mfma(const GemmArgs& g, hipStream_t stream);

@@ -79,13 +79,24 @@ typedef enum {
 
 typedef enum { BWTA_F32 = 0, BWTA_BF16 = 1, BWTA_I32 = 2 } bwta_dtype;
 
-/* Kernel family for the products.  AUTO picks the fastest; MFMA expands the
- * bit planes to int8 {-1, 0, +1} and multiplies on the int8 matrix cores with
- * int32 accumulation; POPCOUNT evaluates
- *   acc = nnz - 2 * sum_words popcount((w & (mask ^ sign)) | (~w & sign))
- * on the vector ALUs.  Both give the same exact sums; for K <= 64 (one 64-bit
- * word per row) MFMA requests run the popcount kernel. */
-typedef enum { BWTA_ALGO_AUTO = 0, BWTA_ALGO_MFMA = 1, BWTA_ALGO_POPCOUNT = 2 } bwta_algo;
+/* Kernel family for the products.  All give the same exact sums.
+ *   AUTO      picks the fastest (MFMA, or the popcount GEMV for decode M <= 4).
+ *   MFMA      expands the bit planes to FP4 (e2m1) {-1, 0, +1} and multiplies
+ *             on the FP4 matrix cores with unit block scales and fp32
+ *             accumulation; every partial sum is an integer below 2^24, so the
+ *             result is the exact int32 sum.
+ *   POPCOUNT  evaluates acc = nnz - 2 * sum_words popcount((w & (mask ^ sign))
+ *             | (~w & sign)) on the vector ALUs.
+ *   MFMA_I8   expands the planes to int8 {-1, 0, +1} and multiplies on the int8
+ *             matrix cores with int32 accumulation.
+ * For K <= 64 (one 64-bit word per row) the MFMA families run the popcount
+ * kernel. */
+typedef enum {
+  BWTA_ALGO_AUTO = 0,
+  BWTA_ALGO_MFMA = 1,
+  BWTA_ALGO_POPCOUNT = 2,
+  BWTA_ALGO_MFMA_I8 = 3
+} bwta_algo;
 
 int bwta_version(void);
 

@@ -130,7 +130,7 @@ def _linear_case(oracle, M, N, K, bf16=False):
     return x, w, ref
 
 
-@pytest.mark.parametrize("algo", ["mfma", "popcount"])
+@pytest.mark.parametrize("algo", ["mfma", "mfma_i8", "popcount"])
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
 def test_gemm(bw, oracle, M, N, K, algo):
     x, w, ref = _linear_case(oracle, M, N, K)
@@ -151,14 +151,14 @@ def test_gemm_ldy(bw, oracle):
     x, w, ref = _linear_case(oracle, M, N, K)
     a = bw.bwta_ternarize_pack(to_dev(x))
     wp = bw.bwta_pack_weights(to_dev(w))
-    for algo in ["mfma", "popcount"]:
+    for algo in ["mfma", "mfma_i8", "popcount"]:
         out = torch.full((M, 100), -7.0, device="cuda")
         bw.bwta_gemm(a, wp, out_dtype="f32", algo=algo, out=out)
         o = to_host(out)
         assert (o[:, :N] == ref["y"]).all() and (o[:, N:] == -7.0).all()
 
 
-@pytest.mark.parametrize("algo", ["popcount", "mfma", "auto"])
+@pytest.mark.parametrize("algo", ["popcount", "mfma", "mfma_i8", "auto"])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16])
 @pytest.mark.parametrize("N,K", [(1000, 1024), (513, 8192), (300, 28672), (77, 200)])
 def test_gemv(bw, oracle, M, N, K, algo):
@@ -171,7 +171,7 @@ def test_gemv(bw, oracle, M, N, K, algo):
     assert (y.view(np.uint32) == ref["y"].view(np.uint32)).all()
 
 
-@pytest.mark.parametrize("algo", ["mfma", "popcount"])
+@pytest.mark.parametrize("algo", ["mfma", "mfma_i8", "popcount"])
 @pytest.mark.parametrize("H,L,D", [(3, 130, 128), (2, 257, 64), (4, 256, 100)])
 def test_batched_ternary_ternary(bw, oracle, H, L, D, algo):
     rng = np.random.Generator(np.random.PCG64(H * L + D))
@@ -198,7 +198,7 @@ def test_pack_weights_columns_all_heads(bw, oracle):
     assert (to_host(got.alpha) == alpha).all()
 
 
-@pytest.mark.parametrize("algo", ["mfma", "popcount"])
+@pytest.mark.parametrize("algo", ["mfma", "mfma_i8", "popcount"])
 @pytest.mark.parametrize("H,L,D", [(2, 300, 128), (3, 256, 64)])
 def test_batched_ternary_binary(bw, oracle, H, L, D, algo):
     """P V: ternary P [L, L] per head times binary V^T [D, L] per head."""
@@ -236,6 +236,6 @@ def test_empty_and_degenerate(bw, oracle):
     a = bw.bwta_ternarize_pack(to_dev(x))
     wp = bw.bwta_pack_weights(to_dev(w))
     assert (to_host(a.nnz) == 0).all() and (to_host(a.alpha) == 0).all()
-    for algo in ["mfma", "popcount"]:
+    for algo in ["mfma", "mfma_i8", "popcount"]:
         assert (to_host(bw.bwta_gemm(a, wp, algo=algo)) == 0).all()
         assert (to_host(bw.bwta_gemv(a, wp, algo=algo)) == 0).all()
