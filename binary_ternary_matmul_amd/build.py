@@ -24,7 +24,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbwta.so")
 
-SOURCES = ["pack.hip", "gemm_mfma.hip", "gemm_mfma_i8.hip", "gemm_popcount.hip", "bwta_api.cpp"]
+SOURCES = ["pack.hip", "gemm_mfma.hip", "gemm_mfma_i8.hip", "gemm_popcount.hip", "gemv_mfma.hip",
+           "bwta_api.cpp"]
 HEADERS = ["device_common.hpp", "kernels.hpp"]
 ARCH = "gfx950"
 

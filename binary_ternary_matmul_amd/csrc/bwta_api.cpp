@@ -153,10 +153,17 @@ static bwta_status run_product(const bwta::GemmArgs& g, bwta_algo algo, bool gem
                                hipStream_t stream) {
   const int64_t row_bytes = (g.K + 63) / 64 * 8;
   if (algo == BWTA_ALGO_AUTO) {
-    // Decode rows: the popcount GEMV streams the weights once for M <= 4.
-    algo = (gemv && g.M <= 4 && !g.b_mask) ? BWTA_ALGO_POPCOUNT : BWTA_ALGO_MFMA;
+    // Decode: a single activation row costs the popcount GEMV one merge and one
+    // population count per weight word, less than building FP4 operands; from
+    // two rows on the FP4 GEMV, whose cost does not grow with M, is faster.
+    algo = (gemv && g.M <= 1 && !g.b_mask) ? BWTA_ALGO_POPCOUNT : BWTA_ALGO_MFMA;
   }
   hipError_t e;
+  if (gemv && !g.b_mask && (algo == BWTA_ALGO_MFMA || algo == BWTA_ALGO_MFMA_I8)) {
+    // Decode: the skinny FP4 kernel streams the weights once for any M <= 16.
+    e = bwta::launch_gemv_mfma(g, stream);
+    return from_hip(e, "gemv launch");
+  }
   if (algo == BWTA_ALGO_POPCOUNT) {
     if (gemv && !g.b_mask && row_bytes % 16 == 0)
       e = bwta::launch_gemv_popcount(g, stream);

@@ -80,7 +80,8 @@ typedef enum {
 typedef enum { BWTA_F32 = 0, BWTA_BF16 = 1, BWTA_I32 = 2 } bwta_dtype;
 
 /* Kernel family for the products.  All give the same exact sums.
- *   AUTO      picks the fastest (MFMA, or the popcount GEMV for decode M <= 4).
+ *   AUTO      picks the fastest: MFMA, except the popcount GEMV for bwta_gemv
+ *             with M = 1.
  *   MFMA      expands the bit planes to FP4 (e2m1) {-1, 0, +1} and multiplies
  *             on the FP4 matrix cores with unit block scales and fp32
  *             accumulation; every partial sum is an integer below 2^24, so the
@@ -90,7 +91,7 @@ typedef enum { BWTA_F32 = 0, BWTA_BF16 = 1, BWTA_I32 = 2 } bwta_dtype;
  *   MFMA_I8   expands the planes to int8 {-1, 0, +1} and multiplies on the int8
  *             matrix cores with int32 accumulation.
  * For K <= 64 (one 64-bit word per row) the MFMA families run the popcount
- * kernel. */
+ * kernel.  bwta_gemv with MFMA or MFMA_I8 runs the FP4 decode kernel. */
 typedef enum {
   BWTA_ALGO_AUTO = 0,
   BWTA_ALGO_MFMA = 1,
