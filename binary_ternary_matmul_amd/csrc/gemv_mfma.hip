@@ -115,7 +115,8 @@ __device__ __forceinline__ void act_slices(uint32_t m, uint32_t s, uint32_t (&o)
   o[3] = q23 & 0xAAAAAAAAu;
 }
 
-// LDS layout.  Expanded: slot (c, e, lane) at ((c * 4 + e) * 64 + lane) * 16.
+// LDS layout.  Expanded: chunk c, slice e, slot s at ((c * 4 + e) * 64 + s) * 16,
+// plus one cleared chunk.
 // Raw: plane p (0 mask, 1 sign) at p * plane, slot (c, g, m) at
 // ((c * 4 + g) * M + m) * 16 within it, then 32 zeroed bytes.  After either:
 // per wave the 16 row sums T (int), then the S > 1 exchange.
@@ -127,7 +128,7 @@ __host__ __device__ inline LdsLayout lds_layout(bool expanded, int chunks, int M
   LdsLayout l;
   l.plane = (uint32_t)chunks * 4u * (uint32_t)M * 16u;
   l.zero_off = 2 * l.plane;
-  l.t_off = expanded ? (uint32_t)chunks * 4096u : l.zero_off + 32u;
+  l.t_off = expanded ? (uint32_t)(chunks + 1) * 4096u : l.zero_off + 32u;
   l.x_off = l.t_off + kMaxW * 16u * 4u;
   l.total = l.x_off + (S > 1 ? (uint32_t)(S * R) * 64u * 16u : 0u);
   return l;
@@ -175,12 +176,25 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     aa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                        aars, (int)((l_item & 15) * 4), 0, 0));
   }
-  // 2. Staging loads, 16 bytes per plane and unit u = (4c + g) * 16 + m; rows
-  //    m >= M are not read.  blockDim is a multiple of 16, so a thread's units
-  //    all belong to row m = threadIdx.x % 16.
-  const int units = chunks * 64;
+  // 2. Staging loads, 16 bytes per plane and unit u = (m * chunks + c) * 4 + g
+  //    over the M live rows (row-major, so one load instruction reads whole
+  //    64-byte pieces of a row).
+  const int units = chunks * 4 * M;
+  // float quotients are exact after a +-1 fix-up for u < 2^24
+  auto fdiv = [](int u, int d, float inv) {
+    int q = (int)((float)u * inv);
+    q += (q + 1) * d <= u ? 1 : 0;
+    q -= q * d > u ? 1 : 0;
+    return q;
+  };
+  const float inv_c = 1.0f / (float)chunks;
+  auto unit_pos = [&](int u, int& m, int& c, int& gg) {
+    gg = u & 3;
+    const int q = u >> 2;
+    m = fdiv(q, chunks, inv_c);
+    c = q - m * chunks;
+  };
   const int nsu = (units + (int)blockDim.x - 1) / (int)blockDim.x;  // rounds, uniform
-  const int my_m = threadIdx.x & 15;
   const __amdgpu_buffer_rsrc_t mrs = checked_rsrc(a_mask, (uint32_t)M * (uint32_t)row_bytes);
   const __amdgpu_buffer_rsrc_t srs = checked_rsrc(a_sign, (uint32_t)M * (uint32_t)row_bytes);
   v4u sm[kMaxSU], ss[kMaxSU];
@@ -188,8 +202,9 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   for (int k = 0; k < kMaxSU; ++k) {
     if (k < nsu) {
       const int u = (int)threadIdx.x + k * (int)blockDim.x;
-      const int cg = u >> 4;
-      const uint32_t off = u < units && my_m < M ? (uint32_t)(my_m * row_bytes + 16 * cg) : kOOB;
+      int m, c, gg;
+      unit_pos(u, m, c, gg);
+      const uint32_t off = u < units ? (uint32_t)(m * row_bytes + 64 * c + 16 * gg) : kOOB;
       sm[k] = __builtin_amdgcn_raw_buffer_load_b128(mrs, (int)off, 0, 0);
       ss[k] = __builtin_amdgcn_raw_buffer_load_b128(srs, (int)off, 0, 0);
     }
@@ -214,14 +229,20 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   issue(0, c0);
   __builtin_amdgcn_sched_barrier(0);
 
-  // 4. Staging stores (they wait for the staging loads only) and row sums:
-  //    per-thread partials of row my_m, summed over the lanes of one row and
-  //    written per wave.  Units past the first kMaxSU rounds (long rows over
-  //    few waves) are loaded and stored one at a time.
-  int tpart = 0;
+  // 4. Staging stores (they wait for the staging loads only) and row sums T,
+  //    accumulated per wave in its own 16 LDS counters (cleared by the wave
+  //    itself, so no barrier is needed before the adds).  Units past the first
+  //    kMaxSU rounds (long rows over few waves) are loaded and stored one at a
+  //    time.  Expanded operands go to slot g * 16 + (m ^ h(c, g)) of their
+  //    (chunk, e) group, h = 4 (c & 1) + g: the 8 lanes of one store (4 g, 2
+  //    chunks) and of one read (8 rows) hit distinct bank groups.  Lanes of rows
+  //    m >= M read a cleared extra chunk.
+  int* tw = tsum + wid * 16;
+  if (lane < 16) tw[lane] = 0;
   auto stage_unit = [&](int u, v4u vm, v4u vs) {
-    const int cg = u >> 4;
-    const int valid = row_bytes - 16 * cg;  // bytes of this unit inside the row
+    int m, c, gg;
+    unit_pos(u, m, c, gg);
+    const int valid = row_bytes - 64 * c - 16 * gg;  // bytes of this unit inside the row
     if (valid < 16) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
@@ -229,8 +250,10 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
         vs[x] = 4 * x < valid ? vs[x] : 0u;
       }
     }
+    int t = 0;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) tpart += __builtin_popcount(vm[x]) - 2 * __builtin_popcount(vs[x]);
+    for (int x = 0; x < 4; ++x) t += __builtin_popcount(vm[x]) - 2 * __builtin_popcount(vs[x]);
+    atomicAdd(&tw[m], t);
     if constexpr (X) {
       uint32_t o[4][4];
 #pragma unroll
@@ -240,13 +263,13 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e][x] = sl[e];
       }
-      const int c = cg >> 2, gg = cg & 3;
+      const int slot = gg * 16 + (m ^ (((c & 1) << 2) | gg));
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        *reinterpret_cast<v4u*>(smem + ((c * 4 + e) * 64 + gg * 16 + my_m) * 16) =
+        *reinterpret_cast<v4u*>(smem + ((c * 4 + e) * 64 + slot) * 16) =
             v4u{o[e][0], o[e][1], o[e][2], o[e][3]};
-    } else if (my_m < M) {
-      const uint32_t slot = (uint32_t)(cg * M + my_m) * 16u;
+    } else {
+      const uint32_t slot = (uint32_t)((c * 4 + gg) * M + m) * 16u;
       *reinterpret_cast<v4u*>(smem + slot) = vm;
       *reinterpret_cast<v4u*>(smem + L.plane + slot) = vs;
     }
@@ -257,26 +280,30 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     if (k < nsu && u < units) stage_unit(u, sm[k], ss[k]);
   }
   for (int u = (int)threadIdx.x + kMaxSU * (int)blockDim.x; u < units; u += (int)blockDim.x) {
-    const uint32_t off = my_m < M ? (uint32_t)(my_m * row_bytes + 16 * (u >> 4)) : kOOB;
+    int m, c, gg;
+    unit_pos(u, m, c, gg);
+    const uint32_t off = (uint32_t)(m * row_bytes + 64 * c + 16 * gg);
     stage_unit(u, __builtin_amdgcn_raw_buffer_load_b128(mrs, (int)off, 0, 0),
                __builtin_amdgcn_raw_buffer_load_b128(srs, (int)off, 0, 0));
   }
-  tpart += __shfl_xor(tpart, 16, kWave);
-  tpart += __shfl_xor(tpart, 32, kWave);
-  if (lane < 16) tsum[wid * 16 + lane] = tpart;
-  if (!X && threadIdx.x < 2)
-    *reinterpret_cast<v4u*>(smem + L.zero_off + 16 * threadIdx.x) = v4u{0u, 0u, 0u, 0u};
-  lds_barrier();
+  if constexpr (X) {
+    for (int z = threadIdx.x; z < 256; z += blockDim.x)  // the extra chunk
+      *reinterpret_cast<v4u*>(smem + (uint32_t)chunks * 4096u + z * 16) = v4u{0u, 0u, 0u, 0u};
+  } else {
+    if (threadIdx.x < 2)
+      *reinterpret_cast<v4u*>(smem + L.zero_off + 16 * threadIdx.x) = v4u{0u, 0u, 0u, 0u};
+  }
 #pragma unroll
   for (int b = 1; b < kNB; ++b) issue(b, c0 + b * kPF);
   __builtin_amdgcn_sched_barrier(0);
+  lds_barrier();
 
   // 5. Main loop.  Raw B operand of lane (r, g) for chunk c: slot (c, g, r) when
   //    r < M, else the zeroed slot (mask 0 makes every product 0).
   const bool live = r < M;
-  const uint32_t am_base = X ? (uint32_t)lane * 16u : live ? (uint32_t)(g * M + r) * 16u : L.zero_off;
+  const uint32_t am_base = X ? 0u : live ? (uint32_t)(g * M + r) * 16u : L.zero_off;
   const uint32_t as_base = live ? L.plane + am_base : L.zero_off;
-  const uint32_t a_step = X ? 4096u : live ? (uint32_t)(4 * M) * 16u : 0u;
+  const uint32_t a_step = X ? 0u : live ? (uint32_t)(4 * M) * 16u : 0u;
   v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   auto compute = [&](int b, int cb) {
 #pragma unroll
@@ -286,8 +313,12 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
         const uint32_t ao = am_base + (uint32_t)c * a_step;
         v4i bop[4];
         if constexpr (X) {
+          // lane slot of chunk c (rows m >= M: the cleared extra chunk)
+          const uint32_t xo = live ? (uint32_t)c * 4096u +
+                                         (uint32_t)(g * 16 + (r ^ (((c & 1) << 2) | g))) * 16u
+                                   : (uint32_t)chunks * 4096u;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) bop[e] = *reinterpret_cast<const v4i*>(smem + ao + e * 1024);
+          for (int e = 0; e < 4; ++e) bop[e] = *reinterpret_cast<const v4i*>(smem + xo + e * 1024);
         } else {
           const v4u am = *reinterpret_cast<const v4u*>(smem + ao);
           const v4u as = *reinterpret_cast<const v4u*>(smem + as_base + (uint32_t)c * a_step);
