@@ -89,6 +89,33 @@ def time_calls(fn, reps=20, replays=3):
     return time_graph(graph_of(fn, reps), reps, replays)
 
 
+def profiled_traffic(key):
+    """HBM bytes per launch of kernel `key` from the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summaries under profiles/ (a line 'traffic <key> bytes_per_launch=..
+    source=<file> sha256=<hex>'), or None when no summary names the key or its
+    kernel source has changed since the counters were taken."""
+    import glob
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    for path in sorted(glob.glob(os.path.join(root, "profiles", "*.md"))):
+        with open(path) as f:
+            for ln in f:
+                parts = ln.split()
+                if len(parts) < 3 or parts[0] != "traffic" or parts[1] != key:
+                    continue
+                kv = dict(p.split("=", 1) for p in parts[2:] if "=" in p)
+                try:
+                    with open(os.path.join(root, kv["source"]), "rb") as src:
+                        if hashlib.sha256(src.read()).hexdigest() != kv["sha256"]:
+                            return None
+                    return {"bytes": int(kv["bytes_per_launch"]),
+                            "algorithmic_bytes": int(kv["algorithmic_bytes_per_launch"]),
+                            "summary": os.path.relpath(path, root)}
+                except (KeyError, OSError, ValueError):
+                    return None
+    return None
+
+
 def bench_prefill(bw, steps, warmup, M=2048):
     import torch
     from binary_ternary_matmul_amd import inputs
@@ -191,10 +218,21 @@ def bench_gemv(bw, copies=24, reps=4):
             kp = bw.padded_k(lin.K)
             nbytes = lin.N * kp / 8 + 4 * lin.N + M * (2 * kp / 8 + 8) + 4 * M * lin.N
             gbs = nbytes / (us * 1e-6) / 1e9
-            out[f"{lin.name}_M{M}"] = {"N": lin.N, "K": lin.K, "us": round(us, 2),
+            kern = "gemv_popcount_kernel" if M == 1 else "gemv_mfma_kernel"  # algo "auto"
+            tr = profiled_traffic(f"{kern}.{lin.name}.M{M}")
+            out[f"{lin.name}_M{M}"] = {"N": lin.N, "K": lin.K, "kernel": kern, "us": round(us, 2),
                                        "bytes": int(nbytes), "GBps": round(gbs, 1),
-                                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 3)}
+                                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
+                                       "traffic": tr["bytes"] if tr else None}
     out.pop("_w", None)
+    # The decode kernel's roofline on the gate/up shape at M = 4 (FP4 GEMV):
+    # algorithmic bytes per launch over the measured per-launch time.
+    ref = out.get("gate_up_M4")
+    if ref:
+        tr = profiled_traffic("gemv_mfma_kernel.gate_up.M4")
+        out["roofline"] = {"bound": "hbm", "kernel": "gemv_mfma_kernel", "shape": "gate_up_M4",
+                           "achieved": ref["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": ref["hbm_frac"], "traffic": tr["bytes"] if tr else None}
     return out
 
 
@@ -255,7 +293,7 @@ def bench_bert(bw, reps=10):
     return {"layer_tops_incl_ternarize": round(tot_ops / (tot_ms * 1e-3) / 1e12, 1), "per_gemm": res}
 
 
-def cpu_baseline(M=2048, rows=384):
+def cpu_baseline(M=2048, rows=2048):
     """The oracle, untouched, on the first `rows` token rows of the same step."""
     from binary_ternary_matmul_amd import inputs
     from oracle import oracle
@@ -276,6 +314,37 @@ def cpu_baseline(M=2048, rows=384):
                       f"of all seven LLaMA-7B layer GEMMs ({ops / 1e9:.0f} G ops)"}
 
 
+def calibrate_copy(nbytes=256 << 20, reps=3):
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (FETCH_SIZE, WRITE_SIZE) of a profiler run."""
+    import torch
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def profile_gemv(bw, copies=4):
+    """A few cold launches of each decode shape (for profiler counters)."""
+    import torch
+    from binary_ternary_matmul_amd import inputs
+    for M in (1, 4, 16):
+        for lin in inputs.llama70b_decode(M):
+            w = bw.bwta_pack_weights(dev(lin.w()))
+            ws = [w] + [bw.BinaryPlanes(w.sign.clone(), w.alpha.clone(), w.K) for _ in range(copies - 1)]
+            a = bw.bwta_ternarize_pack(dev(lin.x()))
+            y = torch.empty((M, lin.N), dtype=torch.float32, device="cuda")
+            torch.cuda.synchronize()
+            for wi in ws:
+                bw.bwta_gemv(a, wi, "f32", "auto", y)
+            torch.cuda.synchronize()
+            del ws, w
+    print(json.dumps({"profile_gemv": "done", "copies": copies}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +352,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="prefill step only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 256 MiB device copy (profiler byte-counter scale)")
+    ap.add_argument("--profile-gemv", action="store_true",
+                    help="only run a few cold launches of each decode GEMV shape")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -293,8 +366,14 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     import binary_ternary_matmul_amd as bw
     bw.lib()
+    if args.profile_gemv:
+        profile_gemv(bw)
+        return
 
     pre = bench_prefill(bw, args.steps, args.warmup)
     achieved = pre["ops"] / (pre["gemm_ms"] * 1e-3) / 1e12
@@ -324,6 +403,11 @@ def main():
                      "peak": FP4_PEAK_TOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / FP4_PEAK_TOPS, 3), "traffic": None},
     }
+    tr = profiled_traffic("gemm_mfma_kernel")
+    if tr:
+        line["roofline"]["traffic"] = tr["bytes"]
+        line["roofline"]["traffic_algorithmic"] = tr["algorithmic_bytes"]
+        line["roofline"]["traffic_source"] = tr["summary"]
     if not args.quick:
         log("[bench] int8 MFMA variant")
         line["mfma_i8"] = bench_algo(bw, pre, "mfma_i8")
