@@ -1,0 +1,174 @@
+"""GPU parity at the benchmark workloads' full sizes, in the launch configuration
+bench.py times (same entry points, algo and output dtype).
+
+Every packed plane, alpha and nnz is compared in full, bit-exact.  Products:
+  * the single linear (128 x 768 x 768) and the decode GEMVs (M in {1, 4, 16}
+    against 28672 x 8192 and 8192 x 28672 weights) and both attention products
+    are compared in full against the oracle;
+  * the BERT-base and LLaMA-7B prefill GEMMs on a seeded sample of rows x
+    columns (always including the first and last of each), accumulators and
+    bf16 outputs bit-exact, and on every output through two properties any
+    product of t in {-1, 0, +1} with s in {-1, +1} has: |acc[m, n]| <= nnz[m]
+    and acc[m, n] = nnz[m] (mod 2).
+"""
+import os
+
+import numpy as np
+import pytest
+
+from binary_ternary_matmul_amd import inputs
+from tests.helpers import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+THREADS = os.cpu_count() or 1
+
+
+@pytest.fixture(scope="module")
+def bw():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import binary_ternary_matmul_amd as b
+    b.lib()
+    return b
+
+
+def _check_planes(bw, oracle, a, x):
+    t, alpha, nnz = oracle.ternarize(x)
+    assert (to_host(a.mask) == oracle.pack_plane(t, "mask")).all()
+    assert (to_host(a.sign) == oracle.pack_plane(t, "sign")).all()
+    assert (to_host(a.alpha).view(np.uint32) == alpha.view(np.uint32)).all()
+    assert (to_host(a.nnz) == nnz).all()
+    return t, alpha, nnz
+
+
+def _check_weights(bw, oracle, wp, w, transpose=False):
+    s, alpha = oracle.binarize(w, transpose=transpose)
+    assert (to_host(wp.sign) == oracle.pack_plane(s, "sign")).all()
+    assert (to_host(wp.alpha).view(np.uint32) == alpha.view(np.uint32)).all()
+    return s, alpha
+
+
+def _check_properties(acc, nnz):
+    nz = nnz.astype(np.int64)[:, None]
+    assert (np.abs(acc.astype(np.int64)) <= nz).all(), "|acc| > nnz"
+    assert ((acc.astype(np.int64) - nz) % 2 == 0).all(), "acc and nnz differ in parity"
+
+
+def _sample(n, k, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    idx = rng.choice(n, size=min(k, n), replace=False)
+    return np.unique(np.concatenate([idx, [0, n - 1]])).astype(np.int64)
+
+
+def _sampled_linear(bw, oracle, lin, x, algo, out_dtype, seed, rows=192, cols=96):
+    """One bench-shaped linear: planes in full, products on a rows x cols sample
+    plus the properties everywhere."""
+    w = lin.w()
+    a = bw.bwta_ternarize_pack(to_dev(x))
+    wp = bw.bwta_pack_weights(to_dev(w))
+    t, a_alpha, nnz = _check_planes(bw, oracle, a, x)
+    s, w_alpha = _check_weights(bw, oracle, wp, w)
+    del w
+    acc = to_host(bw.bwta_gemm(a, wp, out_dtype="i32", algo=algo))
+    y = to_host(bw.bwta_gemm(a, wp, out_dtype=out_dtype, algo=algo))
+    _check_properties(acc, nnz)
+    R, C = _sample(lin.M, rows, seed), _sample(lin.N, cols, seed + 1)
+    ref_acc = oracle.matmul_i32(t[R], s[C], threads=THREADS)
+    assert (acc[np.ix_(R, C)] == ref_acc).all(), f"{lin.name}: sampled accumulators differ"
+    ref_y = oracle.scale(ref_acc, a_alpha[R], w_alpha[C])
+    if out_dtype == "bf16":
+        assert (y[np.ix_(R, C)] == oracle.to_bf16(ref_y)).all(), f"{lin.name}: bf16 outputs differ"
+    else:
+        assert (y[np.ix_(R, C)].view(np.uint32) == ref_y.view(np.uint32)).all()
+
+
+def test_full_single_linear(bw, oracle):
+    """128 x 768 x 768, fp32 in and out: every output."""
+    (lin,) = inputs.single_linear()
+    x, w = lin.x(), lin.w()
+    ref = oracle.linear(x, w, out="f32")
+    a = bw.bwta_ternarize_pack(to_dev(x))
+    wp = bw.bwta_pack_weights(to_dev(w))
+    _check_planes(bw, oracle, a, x)
+    _check_weights(bw, oracle, wp, w)
+    acc = to_host(bw.bwta_gemm(a, wp, out_dtype="i32", algo="auto"))
+    y = to_host(bw.bwta_gemm(a, wp, out_dtype="f32", algo="auto"))
+    assert (acc == ref["acc"]).all()
+    assert (y.view(np.uint32) == ref["y"].view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("i", range(len(inputs.BERT_SHAPES)))
+def test_full_bert_encoder(bw, oracle, i):
+    """BERT-base linears, M = 4096, fp32 in, bf16 out, algo auto (bench's call)."""
+    lin = inputs.bert_encoder()[i]
+    _sampled_linear(bw, oracle, lin, lin.x(), "auto", "bf16", seed=100 + i)
+
+
+@pytest.mark.parametrize("i", range(len(inputs.LLAMA7B_SHAPES)))
+def test_full_llama7b_prefill(bw, oracle, i):
+    """LLaMA-7B prefill linears, M = 2048, bf16 in and out, algo mfma (bench's call)."""
+    acts, lins = inputs.llama7b_prefill()
+    lin = lins[i]
+    x = acts[inputs.LLAMA7B_INPUTS[lin.name]]()
+    _sampled_linear(bw, oracle, lin, x, "mfma", "bf16", seed=200 + i)
+
+
+@pytest.mark.parametrize("shape", [n for n, _, _ in inputs.LLAMA70B_DECODE_SHAPES])
+def test_full_llama70b_decode(bw, oracle, shape):
+    """Decode GEMV at M = 1, 4, 16 on the full 70B-shaped weights, algo auto,
+    fp32 out: every output."""
+    lins = {M: [l for l in inputs.llama70b_decode(M) if l.name == shape][0] for M in (1, 4, 16)}
+    w = lins[16].w()
+    wp = bw.bwta_pack_weights(to_dev(w))
+    s, w_alpha = _check_weights(bw, oracle, wp, w)
+    del w
+    for M, lin in lins.items():
+        x = lin.x()
+        a = bw.bwta_ternarize_pack(to_dev(x))
+        t, a_alpha, nnz = _check_planes(bw, oracle, a, x)
+        ref_acc = oracle.matmul_i32(t, s, threads=THREADS)
+        acc = to_host(bw.bwta_gemv(a, wp, out_dtype="i32", algo="auto"))
+        assert (acc == ref_acc).all(), f"M={M}: accumulators differ"
+        y = to_host(bw.bwta_gemv(a, wp, out_dtype="f32", algo="auto"))
+        ref_y = oracle.scale(ref_acc, a_alpha, w_alpha)
+        assert (y.view(np.uint32) == ref_y.view(np.uint32)).all(), f"M={M}: outputs differ"
+
+
+def test_full_attention(bw, oracle):
+    """32 heads x 2048 x 128: Q K^T int32 scores in full; P V with P the oracle's
+    softmax of the scaled scores (ternarized on the GPU) and V^T packed per
+    channel in one launch from [L, H*D], fp32 out, in full."""
+    import torch
+    att = inputs.attention()
+    H, L, D = att.heads, att.L, att.d
+    q, k = att.q.reshape(H * L, D), att.k.reshape(H * L, D)
+    qa = bw.bwta_ternarize_pack(to_dev(q))
+    ka = bw.bwta_ternarize_pack(to_dev(k))
+    tq, aq, _ = _check_planes(bw, oracle, qa, q)
+    tk, ak, _ = _check_planes(bw, oracle, ka, k)
+    scores = torch.empty((H, L, L), dtype=torch.int32, device="cuda")
+    bw.bwta_batched_gemm(H, qa, L, ka, L, L, L, "i32", "auto", scores)
+    got = to_host(scores)
+    del scores
+    P = np.empty((H * L, L), np.float32)
+    for h in range(H):
+        rows = slice(h * L, (h + 1) * L)
+        ref = oracle.matmul_i32(tq[rows], tk[rows], threads=THREADS)
+        assert (got[h] == ref).all(), f"scores of head {h} differ"
+        P[rows] = oracle.attention_probs(ref, aq[rows], ak[rows], D)
+    del got
+    vf = np.ascontiguousarray(att.v.transpose(1, 0, 2).reshape(L, H * D))
+    pa = bw.bwta_ternarize_pack(to_dev(P))
+    vb = bw.bwta_pack_weights(to_dev(vf), transpose=True)
+    tp, ap, _ = _check_planes(bw, oracle, pa, P)
+    sv, av = _check_weights(bw, oracle, vb, vf, transpose=True)
+    O = torch.empty((H, L, D), dtype=torch.float32, device="cuda")
+    bw.bwta_batched_gemm(H, pa, L, vb, D, L, D, "f32", "auto", O)
+    out = to_host(O)
+    for h in range(H):
+        rows, chans = slice(h * L, (h + 1) * L), slice(h * D, (h + 1) * D)
+        acc = oracle.matmul_i32(tp[rows], sv[chans], threads=THREADS)
+        ref = oracle.scale(acc, ap[rows], av[chans])
+        assert (out[h].view(np.uint32) == ref.view(np.uint32)).all(), f"P V of head {h} differs"
