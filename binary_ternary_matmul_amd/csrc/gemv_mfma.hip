@@ -338,7 +338,10 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
       }
     }
   };
-  for (int cb = c0; cb < c1; cb += kRing) {
+  // Full revolutions refill their slots; the last one issues nothing, so the
+  // epilogue does not wait behind loads of chunks past the range.
+  int cb = c0;
+  for (; cb + kRing < c1; cb += kRing) {
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
       compute(b, cb + b * kPF);
@@ -346,6 +349,8 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+#pragma unroll
+  for (int b = 0; b < kNB; ++b) compute(b, cb + b * kPF);
 
   // 6. Epilogue.  Element u of the U tile in lane l: activation row m = l % 16,
   //    column n_base + 4 (l / 16) + u; the product is T[m] - 2U.
