@@ -281,7 +281,9 @@ hipError_t launch_gemm_pc_out(const GemmArgs& g, hipStream_t stream) {
 
 template <int MB, int NCH, int OUT>
 hipError_t launch_gemv_cfg(const GemmArgs& g, int m_base, int m_count, hipStream_t stream) {
-  constexpr int R = MB >= 4 ? 4 : 8 / MB;
+  // Four weight rows per wave (4 KiB of loads per 1 KiB chunk column): for
+  // M = 1 this streams faster than 1, 2, 8 or 16 rows per wave.
+  constexpr int R = 4;
   const int64_t row_bytes = (g.K + 63) / 64 * 8;
   const int64_t waves_needed = (g.N + R - 1) / R;
   int64_t blocks = (waves_needed + 3) / 4;
