@@ -171,6 +171,38 @@ def test_gemv(bw, oracle, M, N, K, algo):
     assert (y.view(np.uint32) == ref["y"].view(np.uint32)).all()
 
 
+@pytest.mark.parametrize("algo", ["mfma", "popcount"])
+@pytest.mark.parametrize("M,N,K", [(16, 40, 65536), (13, 21, 40000), (9, 600, 36928),
+                                   (16, 4100, 17000), (6, 33, 64), (2, 17, 129)])
+def test_gemv_launch_paths(bw, oracle, M, N, K, algo):
+    """Decode shapes that take the other launch paths of the FP4 GEMV: raw
+    activation planes (expanded operands do not fit in LDS), activation rows
+    split over several launches (K = 65536 at M = 16), a K split over up to 8
+    waves for few weight rows, ragged K and N, and tiny K."""
+    x, w, ref = _linear_case(oracle, M, N, K, bf16=True)
+    a = bw.bwta_ternarize_pack(to_dev(x))
+    wp = bw.bwta_pack_weights(to_dev(w))
+    acc = to_host(bw.bwta_gemv(a, wp, out_dtype="i32", algo=algo))
+    assert (acc == ref["acc"]).all()
+    y = to_host(bw.bwta_gemv(a, wp, out_dtype="bf16", algo=algo))
+    assert (y == ref["y_bf16"]).all()
+
+
+def test_gemv_ldy(bw, oracle):
+    """Outputs with a leading dimension larger than N keep the gap untouched."""
+    import torch
+    M, N, K = 5, 90, 3000
+    x, w, ref = _linear_case(oracle, M, N, K, bf16=True)
+    a = bw.bwta_ternarize_pack(to_dev(x))
+    wp = bw.bwta_pack_weights(to_dev(w))
+    for algo in ["mfma", "popcount"]:
+        out = torch.full((M, 97), -7.0, device="cuda")
+        bw.bwta_gemv(a, wp, out_dtype="f32", algo=algo, out=out[:, :N])
+        o = to_host(out)
+        assert (o[:, :N].view(np.uint32) == ref["y"].view(np.uint32)).all()
+        assert (o[:, N:] == -7.0).all()
+
+
 @pytest.mark.parametrize("algo", ["mfma", "mfma_i8", "popcount"])
 @pytest.mark.parametrize("H,L,D", [(3, 130, 128), (2, 257, 64), (4, 256, 100)])
 def test_batched_ternary_ternary(bw, oracle, H, L, D, algo):
