@@ -224,6 +224,35 @@ def bench_gemv(bw, copies=24, reps=4):
                                        "bytes": int(nbytes), "GBps": round(gbs, 1),
                                        "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
                                        "traffic": tr["bytes"] if tr else None}
+        # Gate and up of one MLP stacked into one [57344, 8192] weight: one launch
+        # reads both (the same bytes as two launches, half the fixed costs).
+        if M == 1:
+            log("[gemv] packing up 28672x8192 (gate/up stacked)")
+            up = bw.bwta_pack_weights(dev(inputs.llama70b_up_weight()()))
+            out["_w"]["gate_up_fused"] = [
+                bw.BinaryPlanes(torch.cat([g.sign, up.sign]), torch.cat([g.alpha, up.alpha]), g.K)
+                for g in out["_w"]["gate_up"]]
+            del up
+        ws = out["_w"]["gate_up_fused"]
+        lin = [l for l in inputs.llama70b_decode(M) if l.name == "gate_up"][0]
+        a = bw.bwta_ternarize_pack(dev(lin.x()))
+        N2 = 2 * lin.N
+        y = torch.empty((M, N2), dtype=torch.float32, device="cuda")
+
+        def run_fused(a=a, y=y, ws=ws):
+            for wi in ws:
+                bw.bwta_gemv(a, wi, "f32", "auto", y)
+        ms = time_calls(run_fused, reps=reps)
+        us = ms * 1e3 / len(ws)
+        kp = bw.padded_k(lin.K)
+        nbytes = N2 * kp / 8 + 4 * N2 + M * (2 * kp / 8 + 8) + 4 * M * N2
+        gbs = nbytes / (us * 1e-6) / 1e9
+        kern = "gemv_popcount_kernel" if M == 1 else "gemv_mfma_kernel"
+        tr = profiled_traffic(f"{kern}.gate_up_fused.M{M}")
+        out[f"gate_up_fused_M{M}"] = {"N": N2, "K": lin.K, "kernel": kern, "us": round(us, 2),
+                                      "bytes": int(nbytes), "GBps": round(gbs, 1),
+                                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
+                                      "traffic": tr["bytes"] if tr else None}
     out.pop("_w", None)
     # The decode kernel's roofline on the gate/up shape at M = 4 (FP4 GEMV):
     # algorithmic bytes per launch over the measured per-launch time.
@@ -328,9 +357,11 @@ def calibrate_copy(nbytes=256 << 20, reps=3):
 
 
 def profile_gemv(bw, copies=4):
-    """A few cold launches of each decode shape (for profiler counters)."""
+    """A few cold launches of each decode shape, and of gate/up stacked into one
+    [57344, 8192] weight (for profiler counters)."""
     import torch
     from binary_ternary_matmul_amd import inputs
+    up = None
     for M in (1, 4, 16):
         for lin in inputs.llama70b_decode(M):
             w = bw.bwta_pack_weights(dev(lin.w()))
@@ -341,6 +372,17 @@ def profile_gemv(bw, copies=4):
             for wi in ws:
                 bw.bwta_gemv(a, wi, "f32", "auto", y)
             torch.cuda.synchronize()
+            if lin.name == "gate_up":  # then gate and up stacked, one launch
+                if up is None:
+                    up = bw.bwta_pack_weights(dev(inputs.llama70b_up_weight()()))
+                fs = [bw.BinaryPlanes(torch.cat([g.sign, up.sign]), torch.cat([g.alpha, up.alpha]), g.K)
+                      for g in ws]
+                y2 = torch.empty((M, 2 * lin.N), dtype=torch.float32, device="cuda")
+                torch.cuda.synchronize()
+                for wi in fs:
+                    bw.bwta_gemv(a, wi, "f32", "auto", y2)
+                torch.cuda.synchronize()
+                del fs
             del ws, w
     print(json.dumps({"profile_gemv": "done", "copies": copies}), flush=True)
 

@@ -157,6 +157,16 @@ def llama70b_decode(M: int = 1) -> list[Linear]:
     return out
 
 
+def llama70b_up_weight():
+    """The up projection of the same LLaMA2-70B MLP: W [28672, 8192] ~ N(0, 0.015), its
+    own draw (the child after the decode shapes' children of the same seed).  Stacked
+    under the gate weight it gives the [57344, 8192] gate/up matrix one decode launch
+    reads."""
+    ss = np.random.SeedSequence(SEED_BASE + 3).spawn(2 * len(LLAMA70B_DECODE_SHAPES) + 1)
+    name, K, N = LLAMA70B_DECODE_SHAPES[0]
+    return _mk_w(ss[-1], N, K, 0.015)
+
+
 @dataclass
 class Attention:
     heads: int

@@ -2,9 +2,10 @@
 bench.py times (same entry points, algo and output dtype).
 
 Every packed plane, alpha and nnz is compared in full, bit-exact.  Products:
-  * the single linear (128 x 768 x 768) and the decode GEMVs (M in {1, 4, 16}
-    against 28672 x 8192 and 8192 x 28672 weights) and both attention products
-    are compared in full against the oracle;
+  * the single linear (128 x 768 x 768), the decode GEMVs (M in {1, 4, 16}
+    against 28672 x 8192 and 8192 x 28672 weights, and against gate and up
+    stacked into one 57344 x 8192 weight) and both attention products are
+    compared in full against the oracle;
   * the BERT-base and LLaMA-7B prefill GEMMs on a seeded sample of rows x
     columns (always including the first and last of each), accumulators and
     bf16 outputs bit-exact, and on every output through two properties any
@@ -128,6 +129,32 @@ def test_full_llama70b_decode(bw, oracle, shape):
         x = lin.x()
         a = bw.bwta_ternarize_pack(to_dev(x))
         t, a_alpha, nnz = _check_planes(bw, oracle, a, x)
+        ref_acc = oracle.matmul_i32(t, s, threads=THREADS)
+        acc = to_host(bw.bwta_gemv(a, wp, out_dtype="i32", algo="auto"))
+        assert (acc == ref_acc).all(), f"M={M}: accumulators differ"
+        y = to_host(bw.bwta_gemv(a, wp, out_dtype="f32", algo="auto"))
+        ref_y = oracle.scale(ref_acc, a_alpha, w_alpha)
+        assert (y.view(np.uint32) == ref_y.view(np.uint32)).all(), f"M={M}: outputs differ"
+
+
+def test_full_llama70b_gate_up_stacked(bw, oracle):
+    """Gate and up of one 70B MLP stacked into one [57344, 8192] weight (one decode
+    launch for both), M = 1, 4, 16, algo auto, fp32 out: every output."""
+    import torch
+    lins = {M: [l for l in inputs.llama70b_decode(M) if l.name == "gate_up"][0] for M in (1, 4, 16)}
+    wg = lins[16].w()
+    wu = inputs.llama70b_up_weight()()
+    pg, pu = bw.bwta_pack_weights(to_dev(wg)), bw.bwta_pack_weights(to_dev(wu))
+    wp = bw.BinaryPlanes(torch.cat([pg.sign, pu.sign]), torch.cat([pg.alpha, pu.alpha]), pg.K)
+    sg, ag = _check_weights(bw, oracle, pg, wg)
+    su, au = _check_weights(bw, oracle, pu, wu)
+    del wg, wu
+    s = np.concatenate([sg, su])
+    w_alpha = np.concatenate([ag, au])
+    for M, lin in lins.items():
+        x = lin.x()
+        a = bw.bwta_ternarize_pack(to_dev(x))
+        t, a_alpha, _ = _check_planes(bw, oracle, a, x)
         ref_acc = oracle.matmul_i32(t, s, threads=THREADS)
         acc = to_host(bw.bwta_gemv(a, wp, out_dtype="i32", algo="auto"))
         assert (acc == ref_acc).all(), f"M={M}: accumulators differ"
