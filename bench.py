@@ -295,12 +295,31 @@ def bench_attention(bw, reps=5, H=32, L=2048, D=128):
         vb = bw.bwta_pack_weights(Vf, transpose=True)
         bw.bwta_batched_gemm(H, pa, L, vb, D, L, D, "f32", "auto", O)
 
+    # Fused: Q K^T -> softmax -> ternarize P -> P V in one launch (no scores or P
+    # in memory), timed alone on resident planes and with the packing of Q, K, V^T.
+    vb = bw.bwta_pack_weights(Vf, transpose=True)
+    Of = torch.empty((H, L, D), dtype=torch.float32, device="cuda")
+
+    def fused():
+        bw.bwta_attention(qa, ka, vb, H, out=Of)
+
+    def fused_all():
+        bw.bwta_attention(bw.bwta_ternarize_pack(Q), bw.bwta_ternarize_pack(Kt),
+                          bw.bwta_pack_weights(Vf, transpose=True), H, out=Of)
+
     ms_qk = time_calls(qk, reps=reps)
     ms_pv = time_calls(pv, reps=reps)
+    ms_f = time_calls(fused, reps=reps)
+    ms_fa = time_calls(fused_all, reps=reps)
     ops = 2.0 * H * L * L * D
     return {"heads": H, "L": L, "d": D,
             "qk_ms": round(ms_qk, 3), "qk_scores_GBps": round(H * L * L * 4 / (ms_qk * 1e-3) / 1e9, 1),
-            "pv_ms": round(ms_pv, 3), "pv_tops_incl_ternarize_P": round(ops / (ms_pv * 1e-3) / 1e12, 1)}
+            "pv_ms": round(ms_pv, 3), "pv_tops_incl_ternarize_P": round(ops / (ms_pv * 1e-3) / 1e12, 1),
+            "fused_kernel": "attention_kernel", "fused_ms": round(ms_f, 4),
+            "fused_tops": round(2 * ops / (ms_f * 1e-3) / 1e12, 1),
+            "fused_scores_per_s": round(H * L * L / (ms_f * 1e-3), -6),
+            "fused_incl_packing_ms": round(ms_fa, 4),
+            "unfused_over_fused": round((ms_qk + ms_pv) / ms_f, 2)}
 
 
 def bench_bert(bw, reps=10):
@@ -398,6 +417,8 @@ def main():
                     help="only run a 256 MiB device copy (profiler byte-counter scale)")
     ap.add_argument("--profile-gemv", action="store_true",
                     help="only run a few cold launches of each decode GEMV shape")
+    ap.add_argument("--attention", action="store_true",
+                    help="only the attention section (unfused products and the fused call)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -415,6 +436,9 @@ def main():
     bw.lib()
     if args.profile_gemv:
         profile_gemv(bw)
+        return
+    if args.attention:
+        print(json.dumps({"attention": bench_attention(bw)}), flush=True)
         return
 
     pre = bench_prefill(bw, args.steps, args.warmup)

@@ -6,10 +6,11 @@ and Efficient Binarized Transformer by Algorithm-Hardware Co-design", Abstract
 (binary weights, ternary activations with tiny values projected to zero,
 bit-packed binary/ternary MatMul for linear and attention operators).
 """
-from ._binding import (BinaryPlanes, BwtaError, TernaryPlanes, bwta_batched_gemm, bwta_gemm,
-                       bwta_gemv, bwta_pack_weights, bwta_ternarize_pack, lib, padded_k,
-                       row_bytes)
+from ._binding import (AttentionProbs, BinaryPlanes, BwtaError, TernaryPlanes, bwta_attention,
+                       bwta_batched_gemm, bwta_gemm, bwta_gemv, bwta_pack_weights,
+                       bwta_ternarize_pack, lib, padded_k, row_bytes)
 
-__all__ = ["BinaryPlanes", "BwtaError", "TernaryPlanes", "bwta_batched_gemm", "bwta_gemm",
+__all__ = ["AttentionProbs", "BinaryPlanes", "BwtaError", "TernaryPlanes", "bwta_attention",
+           "bwta_batched_gemm", "bwta_gemm",
            "bwta_gemv", "bwta_pack_weights", "bwta_ternarize_pack", "lib", "padded_k",
            "row_bytes"]

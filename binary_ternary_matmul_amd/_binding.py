@@ -64,6 +64,9 @@ def lib() -> ctypes.CDLL:
     L.bwta_batched_gemm.restype = I32
     L.bwta_batched_gemm.argtypes = [I64, P, P, P, P, I64, P, P, P, I64, I64, I64, I64, P, I32,
                                     I64, I64, I32, P]
+    L.bwta_attention.restype = I32
+    L.bwta_attention.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, ctypes.c_float, P, I32,
+                                 P, P, P, P, P]
     _lib = L
     return L
 
@@ -195,3 +198,50 @@ def bwta_batched_gemm(batch: int, a: TernaryPlanes, a_batch_rows: int, b, b_batc
                                    out.stride(1), out.stride(0), ALGOS[algo], _stream()),
            "bwta_batched_gemm")
     return out
+
+
+class AttentionProbs(NamedTuple):
+    """P of a fused attention call and its ternarization: p [heads * L, L] fp32,
+    mask [heads * L, row_bytes(L)] uint8, alpha [heads * L] fp32, nnz int32."""
+    p: torch.Tensor
+    mask: torch.Tensor
+    alpha: torch.Tensor
+    nnz: torch.Tensor
+
+
+def bwta_attention(q: TernaryPlanes, k: TernaryPlanes, v: BinaryPlanes, heads: int,
+                   scale: Optional[float] = None, out_dtype: str = "f32",
+                   out: Optional[torch.Tensor] = None, probs: bool = False):
+    """Fused attention: Q, K ternary [heads * L, D] planes, v = V^T binary planes
+    [heads * D, L] (bwta_pack_weights(V [L, heads * D], transpose=True)).
+    scale defaults to 1 / sqrt(D).  Returns O [heads, L, D], and with probs=True
+    also the AttentionProbs the kernel computed on the way."""
+    D = q.K
+    rows = q.mask.shape[0]
+    if heads <= 0 or rows % heads:
+        raise ValueError("q rows must be heads * L")
+    L = rows // heads
+    if k.K != D or k.mask.shape[0] != rows:
+        raise ValueError("k must match q: [heads * L, D]")
+    if v.K != L or v.sign.shape[0] != heads * D:
+        raise ValueError("v must be V^T planes [heads * D, L]")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    dev = q.mask.device
+    if out is None:
+        out = torch.empty((heads, L, D), dtype=_OUT_TORCH[out_dtype], device=dev)
+    if tuple(out.shape) != (heads, L, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [heads, L, D] tensor")
+    pr = None
+    if probs:
+        pr = AttentionProbs(torch.empty((rows, L), dtype=torch.float32, device=dev),
+                            torch.empty((rows, row_bytes(L)), dtype=torch.uint8, device=dev),
+                            torch.empty(rows, dtype=torch.float32, device=dev),
+                            torch.empty(rows, dtype=torch.int32, device=dev))
+    _check(lib().bwta_attention(heads, L, D, _ptr(q.mask), _ptr(q.sign), _ptr(q.alpha),
+                                _ptr(k.mask), _ptr(k.sign), _ptr(k.alpha), _ptr(v.sign),
+                                _ptr(v.alpha), ctypes.c_float(scale), _ptr(out),
+                                DTYPES[out_dtype], _ptr(pr.p if pr else None),
+                                _ptr(pr.mask if pr else None), _ptr(pr.alpha if pr else None),
+                                _ptr(pr.nnz if pr else None), _stream()), "bwta_attention")
+    return (out, pr) if probs else out

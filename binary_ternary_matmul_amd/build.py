@@ -25,7 +25,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbwta.so")
 
 SOURCES = ["pack.hip", "gemm_mfma.hip", "gemm_mfma_i8.hip", "gemm_popcount.hip", "gemv_mfma.hip",
-           "bwta_api.cpp"]
+           "attention.hip", "bwta_api.cpp"]
 HEADERS = ["device_common.hpp", "kernels.hpp"]
 ARCH = "gfx950"
 

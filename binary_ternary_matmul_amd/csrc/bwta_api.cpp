@@ -1,10 +1,12 @@
 // bwta_api.cpp - the extern "C" entry points of libbwta.so: argument
 // validation, status codes, kernel selection.  Definitions of the operations
-// are in bwta.h; the kernels are in pack.hip, gemm_mfma.hip, gemm_popcount.hip.
+// are in bwta.h; the kernels are in pack.hip, gemm_mfma.hip, gemm_mfma_i8.hip,
+// gemm_popcount.hip, gemv_mfma.hip and attention.hip.
 #include "bwta.h"
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -224,6 +226,41 @@ bwta_status bwta_batched_gemm(int64_t batch, const uint8_t* a_mask, const uint8_
   bwta::GemmArgs g{a_mask, a_sign, a_alpha, a_nnz, a_batch_rows, b_mask, b_sign, b_alpha,
                    b_batch_rows, batch, M, N, K, Y, elt(y_dtype), ldy, y_batch_stride};
   return run_product(g, algo, false, static_cast<hipStream_t>(stream));
+}
+
+bwta_status bwta_attention(int64_t heads, int64_t L, int64_t D, const uint8_t* q_mask,
+                           const uint8_t* q_sign, const float* q_alpha, const uint8_t* k_mask,
+                           const uint8_t* k_sign, const float* k_alpha, const uint8_t* v_sign,
+                           const float* v_alpha, float scale, void* O, bwta_dtype o_dtype,
+                           float* p_out, uint8_t* p_mask, float* p_alpha, int32_t* p_nnz,
+                           void* stream) {
+  if (heads < 0 || L < 0 || D < 0)
+    return fail(BWTA_ERR_INVALID, "negative size heads=%lld L=%lld D=%lld", (long long)heads,
+                (long long)L, (long long)D);
+  if (!valid_io_dtype(o_dtype)) return fail(BWTA_ERR_INVALID, "bad output dtype %d", (int)o_dtype);
+  if (!std::isfinite(scale))
+    return fail(BWTA_ERR_INVALID, "scale is not finite");
+  if (heads == 0) return BWTA_OK;
+  if (D != 128) return fail(BWTA_ERR_UNSUPPORTED, "head dim %lld (only 128)", (long long)D);
+  if (L != 512 && L != 1024 && L != 2048)
+    return fail(BWTA_ERR_UNSUPPORTED, "L = %lld (only 512, 1024, 2048)", (long long)L);
+  if (heads > 65535) return fail(BWTA_ERR_UNSUPPORTED, "heads > 65535");
+  BWTA_TRY(check_plane(q_mask, "q_mask"));
+  BWTA_TRY(check_plane(q_sign, "q_sign"));
+  BWTA_TRY(check_plane(q_alpha, "q_alpha"));
+  BWTA_TRY(check_plane(k_mask, "k_mask"));
+  BWTA_TRY(check_plane(k_sign, "k_sign"));
+  BWTA_TRY(check_plane(k_alpha, "k_alpha"));
+  BWTA_TRY(check_plane(v_sign, "v_sign"));
+  BWTA_TRY(check_plane(v_alpha, "v_alpha"));
+  BWTA_TRY(check_plane(O, "O"));
+  if (p_out && !aligned(p_out, 16)) return fail(BWTA_ERR_ALIGN, "p_out is not 16-byte aligned");
+  if (p_mask && !aligned(p_mask, 16)) return fail(BWTA_ERR_ALIGN, "p_mask is not 16-byte aligned");
+  BWTA_TRY(check_word(p_alpha, false, "p_alpha"));
+  BWTA_TRY(check_word(p_nnz, false, "p_nnz"));
+  bwta::AttentionArgs a{heads, L, D, q_mask, q_sign, q_alpha, k_mask, k_sign, k_alpha, v_sign,
+                        v_alpha, scale, O, elt(o_dtype), p_out, p_mask, p_alpha, p_nnz};
+  return from_hip(bwta::launch_attention(a, static_cast<hipStream_t>(stream)), "attention launch");
 }
 
 }  // extern "C"

@@ -42,4 +42,27 @@ hipError_t launch_gemm_popcount(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemv_popcount(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemv_mfma(const GemmArgs& g, hipStream_t stream);
 
+// Fused attention (attention.hip): ternary Q, K planes [heads * L, 16 bytes],
+// binary V^T planes [heads * D, L / 8 bytes], O [heads * L, D].
+struct AttentionArgs {
+  int64_t heads, L, D;
+  const uint8_t* q_mask;
+  const uint8_t* q_sign;
+  const float* q_alpha;
+  const uint8_t* k_mask;
+  const uint8_t* k_sign;
+  const float* k_alpha;
+  const uint8_t* v_sign;
+  const float* v_alpha;
+  float scale;
+  void* O;
+  Elt o_dt;
+  float* p_out;      // optional
+  uint8_t* p_mask;   // optional
+  float* p_alpha;    // optional
+  int32_t* p_nnz;    // optional
+};
+
+hipError_t launch_attention(const AttentionArgs& a, hipStream_t stream);
+
 }  // namespace bwta

@@ -166,6 +166,39 @@ bwta_status bwta_batched_gemm(int64_t batch, const uint8_t* a_mask, const uint8_
                               bwta_dtype y_dtype, int64_t ldy, int64_t y_batch_stride,
                               bwta_algo algo, void* stream);
 
+/* Fused attention (page: Abstract and "Core claim", binary/ternary MatMul for
+ * the attention operators).  For every head h < heads and query row i < L, in
+ * one launch:
+ *   S[j]  = sum_d t_q[i, d] t_k[j, d] over d < D      (ternary x ternary)
+ *   P[j]  = softmax over j < L of alpha_q[i] alpha_k[j] S[j] * scale, in fp32:
+ *           u = S * alpha_k[j]; a = alpha_q[i] * scale * log2(e);
+ *           e_j = exp2(fma(a, u_j, -(a * max u))); p_j = e_j * (1 / sum e)
+ *   t_p, alpha_p, nnz_p = ternarize(P row) by the rule of bwta_ternarize_pack
+ *           (tree(|p|) / L, threshold 0.5 * mu, alpha over the kept values)
+ *   O[i, c] = fl32((nnz_p - 2 sum_j t_p[j] b_v[c, j]) * fl32(alpha_p * alpha_v[c]))
+ *           for every channel c < D, with b_v the V^T sign bits (1 = negative).
+ * The scores and P stay on chip; only O is written unless the optional
+ * outputs are given.
+ * q_mask, q_sign, k_mask, k_sign: heads * L rows of row_bytes(D) bytes (as
+ *    written by bwta_ternarize_pack for [heads * L, D] inputs), 16-byte aligned;
+ *    q_alpha, k_alpha: heads * L floats, 16-byte aligned (nnz is not needed).
+ * v_sign: V^T planes, heads * D rows (row h * D + c = channel c of head h) of
+ *    row_bytes(L) bytes, as written by bwta_pack_weights with stride_row = 1
+ *    over a [L, heads * D] V; v_alpha: heads * D floats; both 16-byte aligned.
+ * O: [heads * L, D] row-major, BWTA_F32 or BWTA_BF16, 16-byte aligned.
+ * Optional (NULL: not written), for inspection: p_out [heads * L, L] fp32 (P),
+ *    p_mask [heads * L, row_bytes(L)] (t_p; its sign plane is all zero since
+ *    every p >= 0), p_alpha [heads * L] floats, p_nnz [heads * L] int32;
+ *    16-byte aligned (p_alpha, p_nnz: 4-byte).
+ * Supported shapes: D = 128 and L in {512, 1024, 2048}, heads <= 65535; other
+ * shapes return BWTA_ERR_UNSUPPORTED.  heads = 0 is a no-op. */
+bwta_status bwta_attention(int64_t heads, int64_t L, int64_t D, const uint8_t* q_mask,
+                           const uint8_t* q_sign, const float* q_alpha, const uint8_t* k_mask,
+                           const uint8_t* k_sign, const float* k_alpha, const uint8_t* v_sign,
+                           const float* v_alpha, float scale, void* O, bwta_dtype o_dtype,
+                           float* p_out, uint8_t* p_mask, float* p_alpha, int32_t* p_nnz,
+                           void* stream);
+
 const char* bwta_status_string(bwta_status status);
 const char* bwta_last_error(void);
 

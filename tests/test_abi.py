@@ -131,6 +131,34 @@ def test_batched_validation(L):
     assert call(a_nnz=0, b_mask=0, K=0) == INVALID
 
 
+def test_attention_validation(L):
+    P = ctypes.c_void_p
+    f = L.bwta_attention
+
+    def call(heads=2, Lk=2048, D=128, q_mask=A, k_alpha=A, v_sign=A, O=A, dt=0, scale=0.088,
+             p_out=0, p_mask=0, p_alpha=0, p_nnz=0):
+        return f(heads, Lk, D, P(q_mask), P(A), P(A), P(A), P(A), P(k_alpha), P(v_sign), P(A),
+                 ctypes.c_float(scale), P(O), dt, P(p_out), P(p_mask), P(p_alpha), P(p_nnz), P(0))
+    assert call(heads=-1) == INVALID
+    assert call(Lk=-2048) == INVALID
+    assert call(dt=2) == INVALID                     # int32 output is not offered
+    assert call(scale=float("inf")) == INVALID
+    assert call(scale=float("nan")) == INVALID
+    assert call(heads=0) == OK                       # no-op before any pointer is examined
+    assert call(heads=0, q_mask=0, O=0) == OK
+    assert call(D=64) == UNSUPPORTED
+    assert call(Lk=4096) == UNSUPPORTED
+    assert call(Lk=1000) == UNSUPPORTED
+    assert call(heads=70000) == UNSUPPORTED
+    assert call(q_mask=0) == INVALID
+    assert call(O=0) == INVALID
+    assert call(v_sign=MIS) == ALIGN
+    assert call(k_alpha=MIS) == ALIGN
+    assert call(p_out=MIS) == ALIGN
+    assert call(p_mask=MIS) == ALIGN
+    assert call(p_nnz=A + 2) == ALIGN
+
+
 def test_binding_refuses_host_tensors():
     import torch
     from binary_ternary_matmul_amd import bwta_ternarize_pack

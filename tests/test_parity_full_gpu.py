@@ -2,6 +2,9 @@
 bench.py times (same entry points, algo and output dtype).
 
 Every packed plane, alpha and nnz is compared in full, bit-exact.  Products:
+  * the fused attention call (32 x 2048 x 128): O, the P planes, alpha_p and
+    nnz_p of every head exactly on the kernel's own P, and P against the fp64
+    softmax on three heads (tests/test_attention_gpu.py states the checks);
   * the single linear (128 x 768 x 768), the decode GEMVs (M in {1, 4, 16}
     against 28672 x 8192 and 8192 x 28672 weights, and against gate and up
     stacked into one 57344 x 8192 weight) and both attention products are
@@ -199,3 +202,9 @@ def test_full_attention(bw, oracle):
         acc = oracle.matmul_i32(tp[rows], sv[chans], threads=THREADS)
         ref = oracle.scale(acc, ap[rows], av[chans])
         assert (out[h].view(np.uint32) == ref.view(np.uint32)).all(), f"P V of head {h} differs"
+
+
+def test_full_fused_attention(bw, oracle):
+    """bwta_attention at 32 heads x 2048 x 128, fp32 out (bench's call)."""
+    from tests.test_attention_gpu import check_attention
+    check_attention(bw, oracle, 32, 2048, threads=THREADS, p_heads=(0, 13, 31))
