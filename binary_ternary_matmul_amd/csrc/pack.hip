@@ -21,11 +21,13 @@
 // 32 lanes per row, several rows per wave.  The row stays in registers between
 // the two passes (sum, then threshold), so x is read from HBM once.
 //
-// Column kernel.  Packing the columns of a row-major [K, C] matrix (V^T for
-// attention) gives each lane one column: a wave-wide load reads 64 adjacent
-// columns of one row (contiguous), a lane folds its column's runs of 8 values
-// into the pairwise tree with a register stack (a binary counter over the run
-// index), and W waves split K into aligned power-of-two ranges.
+// Column kernels.  Packing the columns of a row-major [K, C] matrix (V^T for
+// attention) gives each lane one column, folds its column's aligned runs into
+// the pairwise tree with a register stack (a binary counter over the run
+// index), and lets 16 waves split K into aligned power-of-two ranges.  The
+// staged kernel brings 64 KiB tiles through LDS with 16-byte loads (one
+// memory round trip per 16 x 32 rows, the next tile in flight); the per-lane
+// kernel, for the remaining shapes, reads its column element by element.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -33,6 +35,13 @@ namespace bwta {
 namespace {
 
 constexpr int RUN = 8;  // elements per lane run = bits per stored plane byte
+
+// Workgroup barrier ordering LDS only (global loads in flight are not awaited).
+__device__ __forceinline__ void lds_barrier_local() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 template <typename T>
 struct Raw {
@@ -365,6 +374,108 @@ pack_columns_kernel(const T* __restrict__ X, int64_t C, int64_t K, int64_t ld, i
   }
 }
 
+// Staged column kernel (fast path: 16-byte aligned rows, C a multiple of the
+// 16-byte vector, padded length P >= 16 S).  A block of 16 waves packs 64
+// columns.  Wave w owns the aligned range [w P/16, (w+1) P/16) of the padded
+// length, cut into segments of S rows (S = 32 for bf16, 16 for fp32); in chunk
+// q the block loads segment q of all 16 ranges (16 S rows x 64 columns, 64 KiB)
+// with 16-byte loads into LDS, and lane c of wave w reads its column of its
+// segment from there: the segment is an aligned sub-tree, folded into the
+// wave's binary-counter stack like the runs above, and its S sign bits are S/8
+// whole bytes of the plane.  The next chunk's loads are in flight while the
+// current one is reduced.
+template <typename T>
+struct ColStage {
+  static constexpr int S = sizeof(T) == 2 ? 32 : 16;  // rows per segment
+  static constexpr int VPR = 64 * (int)sizeof(T) / 16;  // 16-byte vectors per tile row
+  static constexpr int UNITS = 16 * S * VPR / 1024;      // vectors per thread per chunk
+};
+
+template <typename T>
+__global__ void __launch_bounds__(1024)
+pack_columns_staged_kernel(const T* __restrict__ X, int64_t C, int64_t K, int64_t ld, int64_t P,
+                           int64_t row_bytes, uint8_t* __restrict__ sign,
+                           float* __restrict__ alpha) {
+  constexpr int S = ColStage<T>::S, VPR = ColStage<T>::VPR, UNITS = ColStage<T>::UNITS;
+  constexpr int EPV = 16 / (int)sizeof(T);  // elements per vector
+  __shared__ __attribute__((aligned(16))) T tile[16 * S][64];
+  __shared__ float red[16][64];
+  const int lane = __lane_id();
+  const int wid = threadIdx.x / kWave;
+  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  const int64_t c = c0 + lane;
+  const bool live = c < C;
+  const int64_t span = P / 16;
+  const int64_t nchunks = span / S;
+
+  auto fetch = [&](int64_t q, u32x4 (&buf)[UNITS]) {
+#pragma unroll
+    for (int i = 0; i < UNITS; ++i) {
+      const int u = i * 1024 + (int)threadIdx.x;
+      const int rr = u / VPR, v = u % VPR;
+      const int64_t k = (int64_t)(rr / S) * span + q * S + rr % S;
+      const int64_t col = c0 + (int64_t)v * EPV;
+      buf[i] = (k < K && col < C) ? *reinterpret_cast<const u32x4*>(X + k * ld + col)
+                                  : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  u32x4 buf[UNITS];
+  fetch(0, buf);
+
+  float stack[kStack];
+#pragma unroll
+  for (int l = 0; l < kStack; ++l) stack[l] = 0.0f;
+  for (int64_t q = 0; q < nchunks; ++q) {
+    lds_barrier_local();  // the previous chunk's tile has been read
+#pragma unroll
+    for (int i = 0; i < UNITS; ++i) {
+      const int u = i * 1024 + (int)threadIdx.x;
+      *reinterpret_cast<u32x4*>(&tile[u / VPR][(u % VPR) * EPV]) = buf[i];
+    }
+    if (q + 1 < nchunks) fetch(q + 1, buf);
+    lds_barrier_local();
+    float v[S];
+    uint32_t sb = 0;
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const uint32_t ux = sizeof(T) == 4 ? raw_bits(tile[wid * S + j][lane])
+                                         : raw_bits(tile[wid * S + j][lane]) << 16;
+      v[j] = __uint_as_float(ux & 0x7FFFFFFFu);
+      sb |= neg_bit(ux) << j;
+    }
+    float node = lane_tree<S>(v);
+    bool open = true;
+#pragma unroll
+    for (int l = 0; l < kStack; ++l) {
+      const bool merge = open && ((q >> l) & 1);
+      if (merge) node = stack[l] + node;
+      if (open && !merge) {
+        stack[l] = node;
+        open = false;
+      }
+    }
+    const int64_t b0 = ((int64_t)wid * span + q * S) / 8;  // first plane byte of the segment
+    if (live && b0 < row_bytes) {
+      if constexpr (S == 32)
+        *reinterpret_cast<uint32_t*>(sign + c * row_bytes + b0) = sb;
+      else
+        *reinterpret_cast<uint16_t*>(sign + c * row_bytes + b0) = (uint16_t)sb;
+    }
+  }
+  float root = 0.0f;
+#pragma unroll
+  for (int l = 0; l < kStack; ++l)
+    if ((nchunks >> l) & 1) root = stack[l] + root;
+  red[wid][lane] = root;
+  __syncthreads();
+  if (wid == 0 && live) {
+    float t[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) t[q] = red[q][lane];
+    alpha[c] = lane_tree<16>(t) / (float)K;
+  }
+}
+
 struct Plan {
   int lpr;    // lanes per row (16, 32 or 64)
   int gpw;    // groups per wave
@@ -447,6 +558,13 @@ hipError_t launch_columns(const T* X, int64_t C, int64_t K, int64_t ld, uint8_t*
   while (P < K) P <<= 1;
   const int64_t row_bytes = (K + 63) / 64 * 8;
   const dim3 grid((unsigned)((C + 63) / 64));
+  constexpr int EPV = 16 / (int)sizeof(T);
+  if (P >= 16 * ColStage<T>::S && C % EPV == 0 && ld % EPV == 0 &&
+      reinterpret_cast<uintptr_t>(X) % 16 == 0 && row_bytes % 4 == 0) {
+    hipLaunchKernelGGL((pack_columns_staged_kernel<T>), grid, dim3(1024), 0, stream, X, C, K, ld,
+                       P, row_bytes, sign, alpha);
+    return hipGetLastError();
+  }
   // W waves split the padded length P; each range must hold whole runs of 8.
   if (P >= 16 * RUN) {
     hipLaunchKernelGGL((pack_columns_kernel<T, 16>), grid, dim3(1024), 0, stream, X, C, K, ld, P,

@@ -104,9 +104,13 @@ def test_pack_weights(bw, oracle, N, K, bf16):
 
 
 @pytest.mark.parametrize("bf16", [False, True])
-@pytest.mark.parametrize("L,C", [(2048, 128), (100, 70), (64, 1)])
+@pytest.mark.parametrize("L,C", [(2048, 128), (100, 70), (64, 1), (1000, 72), (520, 64),
+                                 (300, 8), (4096, 24), (65536, 8)])
 def test_pack_weights_columns(bw, oracle, L, C, bf16):
-    """V^T packing: the columns of a row-major [L, C] matrix become rows."""
+    """V^T packing: the columns of a row-major [L, C] matrix become rows.  The
+    staged kernel takes C a multiple of the 16-byte vector and L >= 512 (bf16)
+    or 256 (fp32) - including ragged L and a partial last block of columns;
+    the others take the per-lane kernel."""
     v = _w(L + C, L, C, bf16)
     got = bw.bwta_pack_weights(to_dev(v), transpose=True)
     s, alpha = oracle.binarize(v, transpose=True)
