@@ -36,6 +36,10 @@ import numpy as np
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POPS
 FP4_PEAK_TOPS = 10100.0      # MI355X dense FP4 MFMA, 10.1 PFLOP/s (the GEMM kernel's dtype)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: 32-bit VALU lane-operations per second
+# (one wave64 instruction takes 4 cycles on a 16-lane SIMD; packed fp32 not counted).
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
+VALU_OPS_PER_SCORE = 11
 
 
 def log(*a):
@@ -319,7 +323,15 @@ def bench_attention(bw, reps=5, H=32, L=2048, D=128):
             "fused_tops": round(2 * ops / (ms_f * 1e-3) / 1e12, 1),
             "fused_scores_per_s": round(H * L * L / (ms_f * 1e-3), -6),
             "fused_incl_packing_ms": round(ms_fa, 4),
-            "unfused_over_fused": round((ms_qk + ms_pv) / ms_f, 2)}
+            "unfused_over_fused": round((ms_qk + ms_pv) / ms_f, 2),
+            # The fused kernel is bound by vector-ALU issue: the method's ~11 VALU
+            # operations per score (scale, max, exp argument, exp, sum, normalise,
+            # two tree adds, compare, select) against the chip's lane-operation rate.
+            "fused_roofline": {"bound": "alu", "kernel": "attention_kernel",
+                               "achieved": round(H * L * L * VALU_OPS_PER_SCORE / (ms_f * 1e-3)),
+                               "peak": VALU_PEAK_LANE_OPS, "unit": "lane-op/s",
+                               "frac": round(H * L * L * VALU_OPS_PER_SCORE / (ms_f * 1e-3)
+                                             / VALU_PEAK_LANE_OPS, 3)}}
 
 
 def bench_bert(bw, reps=10):
