@@ -11,13 +11,17 @@ Where the kernel's ternarization and the oracle's (of its own P) disagree, the
 oracle's p must lie within the P bound of the row's threshold.
 
 Bound on |P_gpu - P_ref| / P_ref (log2 units, x = (z - max z) log2 e, Z the
-row's largest |z| log2 e, T = L / 64 values per lane): the scores u = S alpha_k
-and the row factor a = alpha_q * scale * log2 e carry 1 and 3 roundings, the
-exponent argument fma(a, u, -a max u) one more, so the argument is off by at most
-2.5 * 2^-23 |x| + 2^-23 Z; exp2 turns that into a relative error ln 2 times as
-large, and v_exp_f32 adds about 1 ulp; the sum (T sequential adds, 6 tree
-levels) and p = e * (1 / sum) add (T + 10) * 2^-24.  The test allows twice the
-exponent term (the sum's terms carry it too) plus those.
+row's largest |z| log2 e, T = 16 values per lane): the scores u = S alpha_k and
+the row factor a = alpha_q * scale * log2 e carry 1 and 3 roundings; each wave
+exponentiates fma(a, u, -a m_w) against its own maximum m_w and the waves are
+brought to the row maximum m by f_w = exp2(fma(a, m_w, -a m)), so the exponent
+of e * f_w is off by at most (1.5 * 2^-23 + 2^-24) |x| (the factor a, and the two
+fma roundings, whose arguments add up to |x|) plus 1.5 * 2^-23 Z (u and the two
+products a * m rounded); exp2 turns that into a relative error ln 2 times as
+large, and the two v_exp_f32 add about 1 ulp each; the sum (T sequential adds,
+up to 7 tree levels, the products s_w f_w) and p = e * (f_w / s) add
+(T + 12) * 2^-24.  The test allows twice the exponent term (the sum's terms
+carry it too) plus those.
 """
 import math
 
@@ -58,9 +62,9 @@ def _p_bound(acc, aq, ak, head_dim, L):
     z = aq.astype(np.float64)[:, None] * ak.astype(np.float64)[None] * acc / math.sqrt(head_dim)
     x = (z - z.max(axis=1, keepdims=True)) * LOG2E
     Z = np.abs(z).max(axis=1, keepdims=True) * LOG2E
-    T = L // 64
-    return 2 * math.log(2) * (2.5 * 2.0 ** -23 * np.abs(x) + 2.0 ** -23 * Z + 2.0 ** -23) \
-        + (T + 10) * 2.0 ** -24
+    T = 16
+    return 2 * math.log(2) * (2.5 * 2.0 ** -23 * np.abs(x) + 1.5 * 2.0 ** -23 * Z
+                              + 2 * 2.0 ** -23) + (T + 12) * 2.0 ** -24
 
 
 def check_attention(bw, oracle, H, L, out_dtype="f32", head_dim=D, zero_q_rows=(),
