@@ -31,6 +31,13 @@
  *                  the unpacked values; no popcount anywhere in this file)
  *   epilogue       y = fl32((float)acc * fl32(alpha_a[m] * alpha_b[n]))
  *                  bf16(y) = round-to-nearest-even of the fp32 bits
+ *   residual       (two binary planes per weight row; BiLLM page, Approach:
+ *   binarize       salient weights get a residual, second-order binarization)
+ *                  s1, alpha1 = binarize(w); r = fl32(w - alpha1 * s1), i.e.
+ *                  w - alpha1 where s1 = +1 and w + alpha1 where s1 = -1;
+ *                  s2, alpha2 = binarize(r)   so  w ~ alpha1 s1 + alpha2 s2
+ *   residual       y = fl32(fl32((float)acc1 * fl32(alpha_a * alpha1))
+ *   epilogue              + fl32((float)acc2 * fl32(alpha_a * alpha2)))
  *
  * Build: gcc -O2 -ffp-contract=off (no fast-math) so that every float
  * operation is one IEEE-754 binary32 operation, round-to-nearest-even.
@@ -102,6 +109,29 @@ int oracle_binarize(const float* W, int64_t rows, int64_t K, int64_t stride_row,
   }
   free(a);
   return ORACLE_OK;
+}
+
+/* Residual (two-plane) binarization: the first plane and scale as
+ * oracle_binarize, the second plane and scale those of the residual row
+ * r = w - alpha1 * s1 (in fp32). */
+int oracle_binarize_residual(const float* W, int64_t rows, int64_t K, int64_t stride_row,
+                             int64_t stride_k, int8_t* s1, float* alpha1, int8_t* s2,
+                             float* alpha2) {
+  if (rows < 0 || K <= 0) return ORACLE_ERR_ARGS;
+  int st = oracle_binarize(W, rows, K, stride_row, stride_k, s1, alpha1);
+  if (st != ORACLE_OK) return st;
+  float* res = (float*)malloc((size_t)K * sizeof(float));
+  if (!res) return ORACLE_ERR_NOMEM;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t k = 0; k < K; ++k) {
+      float w = W[r * stride_row + k * stride_k];
+      res[k] = s1[r * K + k] < 0 ? w + alpha1[r] : w - alpha1[r];
+    }
+    st = oracle_binarize(res, 1, K, K, 1, s2 + r * K, alpha2 + r);
+    if (st != ORACLE_OK) break;
+  }
+  free(res);
+  return st;
 }
 
 /* Ternary activations, one row at a time; X row r starts at X + r*stride_row. */
@@ -219,6 +249,18 @@ void oracle_scale(const int32_t* acc, const float* alpha_a, const float* alpha_b
     for (int64_t n = 0; n < N; ++n) {
       float s = alpha_a[m] * alpha_b[n];
       y[m * N + n] = (float)acc[m * N + n] * s;
+    }
+}
+
+/* Epilogue of the two-plane product. */
+void oracle_scale_residual(const int32_t* acc1, const int32_t* acc2, const float* alpha_a,
+                           const float* alpha1, const float* alpha2, int64_t M, int64_t N,
+                           float* y) {
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      float y1 = (float)acc1[m * N + n] * (alpha_a[m] * alpha1[n]);
+      float y2 = (float)acc2[m * N + n] * (alpha_a[m] * alpha2[n]);
+      y[m * N + n] = y1 + y2;
     }
 }
 

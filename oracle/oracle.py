@@ -67,6 +67,9 @@ def _load():
         lib.oracle_matmul_i32_pairs.restype = ctypes.c_int
         lib.oracle_matmul_i32_pairs.argtypes = [P, P, I64, P, P, I64, P]
         lib.oracle_scale.argtypes = [P, P, P, I64, I64, P]
+        lib.oracle_binarize_residual.restype = ctypes.c_int
+        lib.oracle_binarize_residual.argtypes = [P, I64, I64, I64, I64, P, P, P, P]
+        lib.oracle_scale_residual.argtypes = [P, P, P, P, P, I64, I64, P]
         lib.oracle_attention_probs.argtypes = [P, P, P, I64, I64, I64, P]
         _lib = lib
         return lib
@@ -136,6 +139,22 @@ def binarize(W: np.ndarray, transpose: bool = False):
     return s, alpha
 
 
+def binarize_residual(W: np.ndarray):
+    """Two binary planes per row of W (BiLLM page, Approach: residual binarization):
+    (s1, alpha1) = binarize(W), then (s2, alpha2) = binarize of the residual
+    r = W - alpha1 * s1 in fp32.  Returns (s1, alpha1, s2, alpha2)."""
+    W = widen(W)
+    assert W.ndim == 2
+    rows, K = W.shape
+    s1 = np.empty((rows, K), np.int8)
+    s2 = np.empty((rows, K), np.int8)
+    a1 = np.empty(rows, np.float32)
+    a2 = np.empty(rows, np.float32)
+    _check(_load().oracle_binarize_residual(_ptr(W), rows, K, K, 1, _ptr(s1), _ptr(a1), _ptr(s2),
+                                            _ptr(a2)), "binarize_residual")
+    return s1, a1, s2, a2
+
+
 def ternarize(X: np.ndarray):
     """Ternary activations of the rows of X.
 
@@ -202,6 +221,23 @@ def scale(acc: np.ndarray, alpha_a: np.ndarray, alpha_b: np.ndarray) -> np.ndarr
     assert alpha_a.shape == (M,) and alpha_b.shape == (N,)
     y = np.empty((M, N), np.float32)
     _load().oracle_scale(_ptr(acc), _ptr(alpha_a), _ptr(alpha_b), M, N, _ptr(y))
+    return y
+
+
+def scale_residual(acc1: np.ndarray, acc2: np.ndarray, alpha_a: np.ndarray,
+                   alpha1: np.ndarray, alpha2: np.ndarray) -> np.ndarray:
+    """y = fl32(fl32(acc1 * fl32(alpha_a * alpha1)) + fl32(acc2 * fl32(alpha_a * alpha2)))."""
+    acc1 = np.ascontiguousarray(acc1, dtype=np.int32)
+    acc2 = np.ascontiguousarray(acc2, dtype=np.int32)
+    alpha_a = np.ascontiguousarray(alpha_a, dtype=np.float32)
+    alpha1 = np.ascontiguousarray(alpha1, dtype=np.float32)
+    alpha2 = np.ascontiguousarray(alpha2, dtype=np.float32)
+    M, N = acc1.shape
+    assert acc2.shape == (M, N) and alpha_a.shape == (M,)
+    assert alpha1.shape == (N,) and alpha2.shape == (N,)
+    y = np.empty((M, N), np.float32)
+    _load().oracle_scale_residual(_ptr(acc1), _ptr(acc2), _ptr(alpha_a), _ptr(alpha1),
+                                  _ptr(alpha2), M, N, _ptr(y))
     return y
 
 

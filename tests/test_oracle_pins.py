@@ -437,3 +437,76 @@ def test_attention_probs_vs_scipy(oracle):
     ref = softmax(z, axis=1)
     assert np.all(np.abs(P - ref) <= 2.0 ** -23 * ref + 1e-45)
     assert np.all(P > 0)
+
+
+# ----------------------------------------------------------------------------
+# Two-plane residual binarization (BiLLM page, Approach: residual, second-order
+# binarization of the salient weights; here applied to whole rows).
+# ----------------------------------------------------------------------------
+
+def test_residual_hand_rows(oracle):
+    """Worked by hand from the definition.
+    [3, -1, 1, -3]: alpha1 = ((3+1)+(1+3))/4 = 2, r = [1, 1, -1, -1], alpha2 = 1,
+    so 2*s1 + 1*s2 rebuilds the row exactly.
+    [0.5, -0.25, -0.0, -0.25]: alpha1 = 0.25 (-0.0 counts as +), r = [0.25, +0.0,
+    -0.25, +0.0] (-0.25 + 0.25 rounds to +0; -0.0 - 0.25 = -0.25),
+    s2 = [+, +, -, +], alpha2 = ((0.25+0)+(0.25+0))/4 = 0.125."""
+    W = np.array([[3, -1, 1, -3], [0.5, -0.25, -0.0, -0.25]], F)
+    s1, a1, s2, a2 = oracle.binarize_residual(W)
+    assert s1.tolist() == [[1, -1, 1, -1], [1, -1, 1, -1]]
+    assert a1.tolist() == [2.0, 0.25]
+    assert s2.tolist() == [[1, 1, -1, -1], [1, 1, -1, 1]]
+    assert a2.tolist() == [1.0, 0.125]
+
+
+def test_residual_constant_magnitude(oracle):
+    """|w| constant along a row: the residual is zero, s2 = +1, alpha2 = 0."""
+    rng = np.random.default_rng(30)
+    W = (np.where(rng.random((5, 96)) < 0.5, -1.0, 1.0) * 0.375).astype(F)
+    s1, a1, s2, a2 = oracle.binarize_residual(W)
+    assert (s1 == np.where(W < 0, -1, 1)).all()
+    assert (a1 == F(0.375)).all()
+    assert (s2 == 1).all() and (a2 == 0).all()
+
+
+@pytest.mark.parametrize("K", [64, 256, 4096])
+def test_residual_recovers_two_plane_rows(oracle, K):
+    """W = alpha1*S1 + alpha2*S2 with dyadic alpha1 > alpha2 > 0 and S2 agreeing with
+    S1 on exactly half of each row: |w| takes alpha1 +- alpha2 equally often, so the
+    mean of |w| is alpha1, the residual is alpha2*S2, and (with dyadic values and K
+    a power of two every tree sum is exact) the planes and scales come back."""
+    rng = np.random.default_rng(K)
+    rows = 6
+    S1 = np.where(rng.random((rows, K)) < 0.5, -1, 1).astype(np.int8)
+    agree = np.zeros((rows, K), bool)
+    for r in range(rows):
+        agree[r, rng.permutation(K)[:K // 2]] = True
+    S2 = np.where(agree, S1, -S1).astype(np.int8)
+    a1 = np.array([2.0 ** -e for e in range(1, rows + 1)], F)
+    a2 = a1 / 4
+    W = (a1[:, None] * S1 + a2[:, None] * S2).astype(F)
+    s1, b1, s2, b2 = oracle.binarize_residual(W)
+    assert (s1 == S1).all() and (s2 == S2).all()
+    assert (b1 == a1).all() and (b2 == a2).all()
+
+
+def test_scale_residual_closed_form(oracle):
+    """acc1 = 3, acc2 = -1, alpha_a = 2, alpha1 = 0.5, alpha2 = 0.25: 3*1 + (-1)*0.5."""
+    y = oracle.scale_residual(np.array([[3]], np.int32), np.array([[-1]], np.int32),
+                              np.array([2], F), np.array([0.5], F), np.array([0.25], F))
+    assert y[0, 0] == F(2.5)
+
+
+def test_residual_linear_vs_float64(oracle):
+    """The two-plane product against numpy's fp64 matmul of the rebuilt weights
+    alpha_a * (t @ (alpha1 s1 + alpha2 s2)^T): within three fp32 roundings."""
+    rng = np.random.default_rng(31)
+    X = rng.standard_t(4, size=(9, 200)).astype(F)
+    W = (rng.standard_normal((13, 200)) * 0.02).astype(F)
+    t, aa, _ = oracle.ternarize(X)
+    s1, a1, s2, a2 = oracle.binarize_residual(W)
+    y = oracle.scale_residual(oracle.matmul_i32(t, s1), oracle.matmul_i32(t, s2), aa, a1, a2)
+    Wr = a1.astype(np.float64)[:, None] * s1 + a2.astype(np.float64)[:, None] * s2
+    ref = aa.astype(np.float64)[:, None] * (t.astype(np.float64) @ Wr.T)
+    mag = aa.astype(np.float64)[:, None] * (np.abs(t).astype(np.float64) @ np.abs(Wr).T)
+    assert np.all(np.abs(y - ref) <= 4 * 2.0 ** -24 * mag + 1e-30)
