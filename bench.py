@@ -196,6 +196,30 @@ def bench_algo(bw, pre, algo, reps=5):
             "fp4_mfma_speedup": round(tot_ms / pre["gemm_ms"], 2), "per_gemm": res}
 
 
+def bench_residual(bw, pre, reps=5):
+    """The same seven GEMMs with two-plane residual weights (bwta_gemm_residual):
+    both planes in one pass; ops counted per plane (twice the single-plane ops)."""
+    import torch
+    from binary_ternary_matmul_amd import inputs
+    acts, lins = inputs.llama7b_prefill(pre["M"])
+    planes = {name: bw.bwta_ternarize_pack(x) for name, x in pre["X"].items()}
+    res, tot_ops, tot_ms = {}, 0.0, 0.0
+    for lin in lins:
+        wr = bw.bwta_pack_weights_residual(dev(lin.w()))
+        a = planes[inputs.LLAMA7B_INPUTS[lin.name]]
+        out = torch.empty((pre["M"], lin.N), dtype=torch.bfloat16, device="cuda")
+        ms = time_calls(lambda a=a, wr=wr, out=out: bw.bwta_gemm_residual(a, wr, "bf16", out),
+                        reps=reps)
+        ops = 2 * 2.0 * pre["M"] * lin.N * lin.K
+        tot_ops += ops
+        tot_ms += ms
+        res[lin.name] = {"us": round(ms * 1e3, 1), "tops": round(ops / (ms * 1e-3) / 1e12, 1),
+                         "vs_one_plane": round(ms / (pre["per_gemm"][lin.name]["us"] * 1e-3), 2)}
+        del wr
+    return {"layer_ms": round(tot_ms, 4), "layer_tops_two_planes": round(tot_ops / (tot_ms * 1e-3) / 1e12, 1),
+            "time_vs_one_plane": round(tot_ms / pre["gemm_ms"], 2), "per_gemm": res}
+
+
 def bench_gemv(bw, copies=24, reps=4):
     """Decode: HBM GB/s with rotating packed-weight copies (> 512 MB per shape)."""
     import torch
@@ -491,6 +515,8 @@ def main():
         line["mfma_i8"] = bench_algo(bw, pre, "mfma_i8")
         log("[bench] popcount variant")
         line["popcount"] = bench_algo(bw, pre, "popcount")
+        log("[bench] two-plane residual weights")
+        line["residual"] = bench_residual(bw, pre)
         log("[bench] gemv")
         line["gemv"] = bench_gemv(bw)
         log("[bench] attention")

@@ -6,11 +6,13 @@ and Efficient Binarized Transformer by Algorithm-Hardware Co-design", Abstract
 (binary weights, ternary activations with tiny values projected to zero,
 bit-packed binary/ternary MatMul for linear and attention operators).
 """
-from ._binding import (AttentionProbs, BinaryPlanes, BwtaError, TernaryPlanes, bwta_attention,
-                       bwta_batched_gemm, bwta_gemm, bwta_gemv, bwta_pack_weights,
+from ._binding import (AttentionProbs, BinaryPlanes, BwtaError, ResidualPlanes, TernaryPlanes,
+                       bwta_attention, bwta_batched_gemm, bwta_gemm, bwta_gemm_residual,
+                       bwta_gemv, bwta_pack_weights, bwta_pack_weights_residual,
                        bwta_ternarize_pack, lib, padded_k, row_bytes)
 
-__all__ = ["AttentionProbs", "BinaryPlanes", "BwtaError", "TernaryPlanes", "bwta_attention",
-           "bwta_batched_gemm", "bwta_gemm",
+__all__ = ["AttentionProbs", "BinaryPlanes", "BwtaError", "ResidualPlanes", "TernaryPlanes",
+           "bwta_attention", "bwta_batched_gemm", "bwta_gemm", "bwta_gemm_residual",
+           "bwta_pack_weights_residual",
            "bwta_gemv", "bwta_pack_weights", "bwta_ternarize_pack", "lib", "padded_k",
            "row_bytes"]

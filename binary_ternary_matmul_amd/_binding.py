@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
     L.bwta_batched_gemm.restype = I32
     L.bwta_batched_gemm.argtypes = [I64, P, P, P, P, I64, P, P, P, I64, I64, I64, I64, P, I32,
                                     I64, I64, I32, P]
+    L.bwta_pack_weights_residual.restype = I32
+    L.bwta_pack_weights_residual.argtypes = [P, I32, I64, I64, I64, P, P, P]
+    L.bwta_gemm_residual.restype = I32
+    L.bwta_gemm_residual.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, I32, I64, P]
     L.bwta_attention.restype = I32
     L.bwta_attention.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, ctypes.c_float, P, I32,
                                  P, P, P, P, P]
@@ -245,3 +249,43 @@ def bwta_attention(q: TernaryPlanes, k: TernaryPlanes, v: BinaryPlanes, heads: i
                                 _ptr(pr.mask if pr else None), _ptr(pr.alpha if pr else None),
                                 _ptr(pr.nnz if pr else None), _stream()), "bwta_attention")
     return (out, pr) if probs else out
+
+
+class ResidualPlanes(NamedTuple):
+    """Two-plane residual binary weights of N rows: sign [2N, row_bytes(K)] uint8
+    and alpha [2N] fp32, interleaved in groups of 32 rows (plane 1 of rows
+    32p..32p+31, then plane 2 of the same rows)."""
+    sign: torch.Tensor
+    alpha: torch.Tensor
+    K: int
+
+
+def bwta_pack_weights_residual(W: torch.Tensor) -> ResidualPlanes:
+    """Two binary planes per row of W [N, K] (N a multiple of 32)."""
+    _dev_check(W, "W")
+    if W.dtype not in (torch.float32, torch.bfloat16) or W.dim() != 2 or W.stride(1) != 1:
+        raise ValueError("W must be a 2-D float32/bfloat16 tensor with unit stride along K")
+    rows, K = W.shape
+    sign = torch.empty((2 * rows, row_bytes(K)), dtype=torch.uint8, device=W.device)
+    alpha = torch.empty(2 * rows, dtype=torch.float32, device=W.device)
+    _check(lib().bwta_pack_weights_residual(_ptr(W), _TORCH_DT[W.dtype], rows, K, W.stride(0),
+                                            _ptr(sign), _ptr(alpha), _stream()),
+           "bwta_pack_weights_residual")
+    return ResidualPlanes(sign, alpha, K)
+
+
+def bwta_gemm_residual(a: TernaryPlanes, w: ResidualPlanes, out_dtype: str = "f32",
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y[M, N] = alpha_a * (alpha1 * (t @ s1^T) + alpha2 * (t @ s2^T))."""
+    if a.K != w.K:
+        raise ValueError(f"K mismatch: activations {a.K}, weights {w.K}")
+    M, N = a.mask.shape[0], w.sign.shape[0] // 2
+    if out is None:
+        out = torch.empty((M, N), dtype=_OUT_TORCH[out_dtype], device=a.mask.device)
+    if out.dim() != 2 or out.shape[0] != M or out.shape[1] < N or out.stride(1) != 1:
+        raise ValueError("out must be [M, >=N] with unit column stride")
+    _check(lib().bwta_gemm_residual(_ptr(a.mask), _ptr(a.sign), _ptr(a.alpha), _ptr(a.nnz),
+                                    _ptr(w.sign), _ptr(w.alpha), M, N, a.K, _ptr(out),
+                                    DTYPES[out_dtype], out.stride(0), _stream()),
+           "bwta_gemm_residual")
+    return out

@@ -195,7 +195,12 @@ __device__ __forceinline__ v16f mfma_fp4(v4i a, v4i b, v16f c) {
 // rows, 64 KiB in all (within the rings whenever S > 1).
 constexpr size_t kXchgBytes = (size_t)TILES * TILES * 16 * kWave * 4;
 
-template <bool B_TERNARY, int OUT, int S>
+// RES: B holds two binary planes per weight row, interleaved in groups of 32
+// rows (plane 1 of weight rows 32p..32p+31, then plane 2 of the same rows), so
+// MFMA column tiles 2jj and 2jj + 1 of a wave tile carry the two accumulators of
+// the same 32 outputs in the same lanes, and the epilogue writes
+// y = acc1 * (alpha_a * alpha1) + acc2 * (alpha_a * alpha2) to N / 2 columns.
+template <bool B_TERNARY, int OUT, int S, bool RES = false>
 __global__ void __launch_bounds__(S * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__ a_sign,
                  const float* __restrict__ a_alpha, int64_t a_batch_rows,
@@ -504,6 +509,14 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     }
   }
 
+  // The tile's scales were stored to LDS by other lanes (wave 0): order those
+  // stores before the reads below.  Without the fence the compiler may move the
+  // reads up across the short main loop of a one-step K (it orders memory per
+  // lane), and lanes would read scales not yet written.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
   // Epilogue straight from the registers of the owned tile rows: y = acc *
   // (alpha_a[row] * alpha_b[col]) in fp32 (the product of the scales first),
   // bf16 rounded to nearest even (v_cvt_pk_bf16_f32), or the int32 sum itself.
@@ -514,7 +527,7 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   typedef uint32_t v2u __attribute__((ext_vector_type(2)));
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));
   constexpr int ES = OUT == (int)Elt::BF16 ? 2 : 4;
-  char* ytile = static_cast<char*>(Y) + (b * y_batch_stride + m0 * ldy + n0) * ES;
+  char* ytile = static_cast<char*>(Y) + (b * y_batch_stride + m0 * ldy + (RES ? n0 / 2 : n0)) * ES;
   // The column scales of this lane's 64 columns, read once.
   float ab[TILES][4][4];
 #pragma unroll
@@ -534,6 +547,77 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   const __amdgpu_buffer_rsrc_t yrs = uniform_rsrc(ytile);
   const uint32_t ldb = (uint32_t)(ldy * ES);
   const uint32_t lane_off = r * ldb + 4 * g * ES;
+  if constexpr (RES) {
+    static_assert(OUT != (int)Elt::I32, "two-plane products are scaled");
+
+    // n_valid is a multiple of 64 (N / 2 a multiple of 32): whole output tiles.
+    // The scales come straight from global memory (L2 hits: wave 0 read them).
+    float ab2[TILES][4][4];
+#pragma unroll
+    for (int j = 0; j < TILES; ++j)
+#pragma unroll
+      for (int qh = 0; qh < 4; ++qh)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int col = 32 * j + 8 * qh + 4 * g + u;
+          ab2[j][qh][u] = col < n_valid ? b_alpha[b * b_batch_rows + n0 + col] : 0.0f;
+        }
+#pragma unroll
+    for (int ii = 0; ii < TPW; ++ii) {
+      const int i = (ii + rot) & 3;
+      const int row = 32 * i + r;
+      const float aa = row < m_valid ? a_alpha[b * a_batch_rows + m0 + row] : 0.0f;
+      uint32_t o[TILES / 2][4][4];
+#pragma unroll
+      for (int jj = 0; jj < TILES / 2; ++jj)
+#pragma unroll
+        for (int qh = 0; qh < 4; ++qh)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float y1 = acc[ii][2 * jj][4 * qh + u] * (aa * ab2[2 * jj][qh][u]);
+            const float y2 = acc[ii][2 * jj + 1][4 * qh + u] * (aa * ab2[2 * jj + 1][qh][u]);
+            const float y = y1 + y2;
+            if constexpr (OUT == (int)Elt::F32)
+              o[jj][qh][u] = __float_as_uint(y);
+            else
+              o[jj][qh][u] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y);
+          }
+      if (full) {
+        const int soff = (int)__builtin_amdgcn_readfirstlane(32 * i * ldb);
+#pragma unroll
+        for (int jj = 0; jj < TILES / 2; ++jj)
+#pragma unroll
+          for (int qh = 0; qh < 4; ++qh) {
+            const int voff = (int)(lane_off + (32 * jj + 8 * qh) * ES);
+            const uint32_t(&w)[4] = o[jj][qh];
+            if constexpr (ES == 4) {
+              const v4u d = {w[0], w[1], w[2], w[3]};
+              __builtin_amdgcn_raw_buffer_store_b128(d, yrs, voff, soff, 0);
+            } else {
+              const v2u d = {w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+              __builtin_amdgcn_raw_buffer_store_b64(d, yrs, voff, soff, 0);
+            }
+          }
+      } else if (row < m_valid) {
+#pragma unroll
+        for (int jj = 0; jj < TILES / 2; ++jj)
+#pragma unroll
+          for (int qh = 0; qh < 4; ++qh)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int col = 32 * jj + 8 * qh + 4 * g + u;
+              if (col < n_valid / 2) {
+                char* yp = ytile + ((int64_t)row * ldy + col) * ES;
+                if constexpr (ES == 4)
+                  *reinterpret_cast<uint32_t*>(yp) = o[jj][qh][u];
+                else
+                  *reinterpret_cast<uint16_t*>(yp) = (uint16_t)o[jj][qh][u];
+              }
+            }
+      }
+    }
+    return;
+  }
   // Per owned row block: every accumulator is read once into the output words
   // (4 consecutive columns per (j, qh)), then stored - wide when the tile is
   // complete, element by element with bounds checks otherwise.
@@ -611,12 +695,12 @@ int choose_split(int64_t tiles, int64_t steps) {
   return best;
 }
 
-template <bool B_TERNARY, int OUT, int S>
+template <bool B_TERNARY, int OUT, int S, bool RES = false>
 hipError_t launch_k(const GemmArgs& g, int64_t row_bytes, int64_t tm, int64_t tn,
                     hipStream_t stream) {
   size_t lds = (size_t)S * kRing * Stage<B_TERNARY>::kBytes;
   if (S > 1 && lds < kXchgBytes) lds = kXchgBytes;
-  auto kfn = gemm_mfma_kernel<B_TERNARY, OUT, S>;
+  auto kfn = gemm_mfma_kernel<B_TERNARY, OUT, S, RES>;
   hipError_t e =
       hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -627,16 +711,16 @@ hipError_t launch_k(const GemmArgs& g, int64_t row_bytes, int64_t tm, int64_t tn
   return hipGetLastError();
 }
 
-template <bool B_TERNARY, int OUT>
+template <bool B_TERNARY, int OUT, bool RES = false>
 hipError_t launch_s(const GemmArgs& g, int S, int64_t row_bytes, int64_t tm, int64_t tn,
                     hipStream_t stream) {
   switch (S) {
     case 1:
-      return launch_k<B_TERNARY, OUT, 1>(g, row_bytes, tm, tn, stream);
+      return launch_k<B_TERNARY, OUT, 1, RES>(g, row_bytes, tm, tn, stream);
     case 2:
-      return launch_k<B_TERNARY, OUT, 2>(g, row_bytes, tm, tn, stream);
+      return launch_k<B_TERNARY, OUT, 2, RES>(g, row_bytes, tm, tn, stream);
     default:
-      return launch_k<B_TERNARY, OUT, 4>(g, row_bytes, tm, tn, stream);
+      return launch_k<B_TERNARY, OUT, 4, RES>(g, row_bytes, tm, tn, stream);
   }
 }
 
@@ -661,6 +745,24 @@ hipError_t launch_b(const GemmArgs& g, hipStream_t stream) {
 
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream) {
   return g.b_mask ? launch_b<true>(g, stream) : launch_b<false>(g, stream);
+}
+
+// Two-plane product: g.N counts plane rows (twice the outputs), g.Y has g.N / 2
+// columns; binary B, fp32 or bf16 output.
+hipError_t launch_gemm_mfma_residual(const GemmArgs& g, hipStream_t stream) {
+  if (g.b_mask || g.N % 64 != 0 || g.y_dt == Elt::I32) return hipErrorInvalidValue;
+  const int64_t row_bytes = (g.K + 63) / 64 * 8;
+  const int64_t tm = (g.M + WAVE_TILE - 1) / WAVE_TILE;
+  const int64_t tn = (g.N + WAVE_TILE - 1) / WAVE_TILE;
+  const int64_t steps = (row_bytes / 8 + 3) / 4;
+  // Twice the tiles of the one-plane product: from 1024 tiles on, splitting K
+  // only adds exchange work (LLaMA-7B gate: 125 us unsplit, 163 / 225 us with
+  // S = 2 / 4).
+  const int64_t tiles = tm * tn * g.batch;
+  const int S = tiles >= 1024 ? 1 : choose_split(tiles, steps);
+  return g.y_dt == Elt::F32
+             ? launch_s<false, (int)Elt::F32, true>(g, S, row_bytes, tm, tn, stream)
+             : launch_s<false, (int)Elt::BF16, true>(g, S, row_bytes, tm, tn, stream);
 }
 
 }  // namespace bwta

@@ -18,6 +18,11 @@ hipError_t launch_ternarize(const void* X, Elt dt, int64_t rows, int64_t K, int6
                             hipStream_t stream);
 hipError_t launch_binarize(const void* W, Elt dt, int64_t rows, int64_t K, int64_t stride_row,
                            int64_t stride_k, uint8_t* sign, float* alpha, hipStream_t stream);
+// Two-plane residual binarization, planes interleaved in groups of 32 rows
+// (rows must be a multiple of 32).
+hipError_t launch_binarize_residual(const void* W, Elt dt, int64_t rows, int64_t K,
+                                   int64_t stride_row, uint8_t* sign, float* alpha,
+                                   hipStream_t stream);
 
 // Common description of one (possibly batched) product.
 struct GemmArgs {
@@ -37,6 +42,8 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
+// Two-plane residual weights (B interleaved in groups of 32 rows, g.N = 2 x outputs).
+hipError_t launch_gemm_mfma_residual(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemm_mfma_i8(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemm_popcount(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemv_popcount(const GemmArgs& g, hipStream_t stream);

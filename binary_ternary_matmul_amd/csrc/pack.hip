@@ -53,12 +53,6 @@ __device__ __forceinline__ uint32_t ebits(const uint32_t* raw, int j, float) { r
 __device__ __forceinline__ uint32_t ebits(const uint32_t* raw, int j, uint16_t) {
   return (raw[j >> 1] >> (16 * (j & 1))) << 16;
 }
-__device__ __forceinline__ float elem(const uint32_t* raw, int j, float t) {
-  return __uint_as_float(ebits(raw, j, t));
-}
-__device__ __forceinline__ float elem(const uint32_t* raw, int j, uint16_t t) {
-  return __uint_as_float(ebits(raw, j, t));
-}
 
 // Decisions as integer arithmetic on the IEEE bit patterns (finite inputs), so
 // no per-element lane masks are formed.  For non-negative floats a, t:
@@ -476,6 +470,103 @@ pack_columns_staged_kernel(const T* __restrict__ X, int64_t C, int64_t K, int64_
   }
 }
 
+// Two-plane residual binarization (BiLLM page, Approach: residual binarization
+// of salient weights; here whole rows): plane 1 and alpha1 as the binary rule,
+// plane 2 and alpha2 the binary rule on r = w - alpha1 * s1 (fp32; the padding
+// stays zero).  One wave per row, four rows per block; lane l owns the aligned
+// range [l E, (l+1) E) of the row padded to 64 E >= max(P, 512) values (zeros
+// past P leave the root unchanged), folds its runs of 8 into a binary-counter
+// stack, and the 64 lane roots meet in a butterfly (lane bit 0 first), so both
+// sums follow the pairwise tree exactly.  Output rows are interleaved in groups
+// of 32: weight row n -> plane row 64 (n / 32) + n % 32 (plane 1), that + 32
+// (plane 2); alpha likewise.
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(256)
+pack_residual_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t sr, int64_t E,
+                     int64_t row_bytes, uint8_t* __restrict__ sign, float* __restrict__ alpha) {
+  const int lane = __lane_id();
+  const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (r >= rows) return;  // whole waves leave together; no block barrier below
+  const T* xrow = X + r * sr;
+  const int64_t out1 = 64 * (r >> 5) + (r & 31), out2 = out1 + 32;
+  const int64_t runs = E / RUN;
+  const int64_t e_lane = (int64_t)lane * E;
+  constexpr int NW = Raw<T>::kWords;
+  auto fetch = [&](int64_t e, uint32_t (&raw)[NW]) {
+    if constexpr (VEC)
+      load_run<T, 1>(xrow, e, K, 1, raw);
+    else
+      load_run<T, 2>(xrow, e, K, 1, raw);
+  };
+  float a1 = 0.0f;
+#pragma unroll 1
+  for (int plane = 0; plane < 2; ++plane) {
+    float stack[kStack];
+#pragma unroll
+    for (int l = 0; l < kStack; ++l) stack[l] = 0.0f;
+    uint8_t* srow = sign + (plane ? out2 : out1) * row_bytes;
+#pragma unroll 1
+    for (int64_t n = 0; n < runs; ++n) {
+      const int64_t e = e_lane + n * RUN;
+      uint32_t raw[NW];
+      fetch(e, raw);
+      float v[RUN];
+      uint32_t sb = 0;
+#pragma unroll
+      for (int j = 0; j < RUN; ++j) {
+        uint32_t ux = ebits(raw, j, T{});
+        if (plane == 1 && e + j < K) {
+          const float x = __uint_as_float(ux);
+          ux = __float_as_uint(neg_bit(ux) ? x + a1 : x - a1);
+        }
+        v[j] = __uint_as_float(ux & 0x7FFFFFFFu);
+        sb |= neg_bit(ux) << j;
+      }
+      float node = lane_tree<RUN>(v);
+      bool open = true;
+#pragma unroll
+      for (int l = 0; l < kStack; ++l) {
+        const bool merge = open && ((n >> l) & 1);
+        if (merge) node = stack[l] + node;
+        if (open && !merge) {
+          stack[l] = node;
+          open = false;
+        }
+      }
+      const int64_t byte = e / 8;
+      if (byte < row_bytes) srow[byte] = (uint8_t)sb;
+    }
+    float root = 0.0f;
+#pragma unroll
+    for (int l = 0; l < kStack; ++l)
+      if ((runs >> l) & 1) root = stack[l] + root;
+#pragma unroll
+    for (int b = 0; b < 6; ++b) root = root + __shfl_xor(root, 1 << b, kWave);
+    const float al = root / (float)K;
+    if (plane == 0) a1 = al;
+    if (lane == 0) alpha[plane ? out2 : out1] = al;
+  }
+}
+
+template <typename T>
+hipError_t launch_residual(const T* X, int64_t rows, int64_t K, int64_t sr, uint8_t* sign,
+                           float* alpha, hipStream_t stream) {
+  int64_t P = 1;
+  while (P < K) P <<= 1;
+  const int64_t E = P / 64 > RUN ? P / 64 : RUN;
+  const int64_t row_bytes = (K + 63) / 64 * 8;
+  const bool vec = K % RUN == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0 &&
+                   (sr * (int64_t)sizeof(T)) % 16 == 0;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (vec)
+    hipLaunchKernelGGL((pack_residual_kernel<T, true>), grid, dim3(256), 0, stream, X, rows, K, sr,
+                       E, row_bytes, sign, alpha);
+  else
+    hipLaunchKernelGGL((pack_residual_kernel<T, false>), grid, dim3(256), 0, stream, X, rows, K,
+                       sr, E, row_bytes, sign, alpha);
+  return hipGetLastError();
+}
+
 struct Plan {
   int lpr;    // lanes per row (16, 32 or 64)
   int gpw;    // groups per wave
@@ -607,6 +698,15 @@ hipError_t launch_ternarize(const void* X, Elt dt, int64_t rows, int64_t K, int6
                             uint8_t* mask, uint8_t* sign, float* alpha, int32_t* nnz,
                             hipStream_t stream) {
   return launch_any<true>(X, dt, rows, K, stride_row, 1, mask, sign, alpha, nnz, stream);
+}
+
+hipError_t launch_binarize_residual(const void* W, Elt dt, int64_t rows, int64_t K,
+                                   int64_t stride_row, uint8_t* sign, float* alpha,
+                                   hipStream_t stream) {
+  return dt == Elt::F32 ? launch_residual<float>(static_cast<const float*>(W), rows, K, stride_row,
+                                                 sign, alpha, stream)
+                        : launch_residual<uint16_t>(static_cast<const uint16_t*>(W), rows, K,
+                                                    stride_row, sign, alpha, stream);
 }
 
 hipError_t launch_binarize(const void* W, Elt dt, int64_t rows, int64_t K, int64_t stride_row,

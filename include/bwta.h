@@ -117,6 +117,21 @@ bwta_status bwta_pack_weights(const void* W, bwta_dtype w_dtype, int64_t rows, i
                               int64_t stride_row, int64_t stride_k, uint8_t* sign,
                               float* alpha, void* stream);
 
+/* Two-plane residual binary weights (BiLLM page, Approach: salient weights get a
+ * residual, second-order binarization; here every row): plane 1 and alpha1 are
+ * bwta_pack_weights' sign plane and scale; plane 2 and alpha2 are the same rule
+ * applied to the fp32 residual r = w - alpha1 * s1 (w - alpha1 where w >= 0 or
+ * w is -0.0, w + alpha1 where w < 0), so w ~ alpha1 s1 + alpha2 s2.
+ * W: rows x K, row r at W + r * stride_row elements (unit stride along k),
+ *    BWTA_F32 or BWTA_BF16; rows a multiple of 32 (else BWTA_ERR_UNSUPPORTED).
+ * sign: out, 2 * rows * row_bytes(K) bytes, 16-byte aligned; the planes are
+ *    interleaved in groups of 32 rows: plane 1 of weight row n is plane row
+ *    64 (n / 32) + n % 32, plane 2 is that row + 32.
+ * alpha: out, 2 * rows floats in the same interleaved order. */
+bwta_status bwta_pack_weights_residual(const void* W, bwta_dtype w_dtype, int64_t rows, int64_t K,
+                                       int64_t stride_row, uint8_t* sign, float* alpha,
+                                       void* stream);
+
 /* Ternary activations, projected online (page: Abstract, ternary activations
  * with tiny values projected to zero, two bits per value).
  * X: rows x K, row r at X + r * stride_row elements, unit stride along k,
@@ -138,6 +153,19 @@ bwta_status bwta_gemm(const uint8_t* a_mask, const uint8_t* a_sign, const float*
                       const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha,
                       int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype, int64_t ldy,
                       bwta_algo algo, void* stream);
+
+/* Prefill linear with two-plane residual weights (w_sign, w_alpha as written by
+ * bwta_pack_weights_residual for N weight rows, 2N plane rows):
+ *   Y[m][n] = fl32(fl32(acc1 * fl32(alpha_a[m] * alpha1[n]))
+ *               + fl32(acc2 * fl32(alpha_a[m] * alpha2[n])))
+ * with acc_i = sum_k t[m][k] * s_i[n][k], both planes multiplied in one pass on
+ * the FP4 matrix cores.  Y: M x N, leading dimension ldy >= N, BWTA_F32 or
+ * BWTA_BF16.  N must be a multiple of 32 and K > 64 (else
+ * BWTA_ERR_UNSUPPORTED); a_nnz is not used and may be NULL. */
+bwta_status bwta_gemm_residual(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
+                               const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha,
+                               int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype,
+                               int64_t ldy, void* stream);
 
 /* Decode GEMV / skinny GEMM, 1 <= M <= 16: the same product as bwta_gemm with
  * kernels that stream the packed weights from HBM once (page: Abstract, lower

@@ -159,6 +159,31 @@ def test_attention_validation(L):
     assert call(p_nnz=A + 2) == ALIGN
 
 
+def test_residual_validation(L):
+    P = ctypes.c_void_p
+    pk = L.bwta_pack_weights_residual
+    assert pk(P(A), 0, 33, 64, 64, P(A), P(A), P(0)) == UNSUPPORTED   # rows not a multiple of 32
+    assert pk(P(A), 5, 32, 64, 64, P(A), P(A), P(0)) == INVALID       # dtype
+    assert pk(P(A), 0, 32, 0, 64, P(A), P(A), P(0)) == INVALID        # K
+    assert pk(P(A), 0, 32, 64, 32, P(A), P(A), P(0)) == INVALID       # stride < K
+    assert pk(P(A), 0, 32, 64, 64, P(MIS), P(A), P(0)) == ALIGN
+    assert pk(P(0), 0, 0, 64, 64, P(0), P(0), P(0)) == OK            # no rows
+    g = L.bwta_gemm_residual
+
+    def call(M=4, N=64, K=128, Y=A, dt=0, ldy=64, w_sign=A, a_nnz=0):
+        return g(P(A), P(A), P(A), P(a_nnz), P(w_sign), P(A), M, N, K, P(Y), dt, ldy, P(0))
+    assert call(N=48) == UNSUPPORTED
+    assert call(K=64) == UNSUPPORTED
+    assert call(M=-1) == INVALID
+    assert call(K=0) == INVALID
+    assert call(dt=2) == INVALID                                      # scaled outputs only
+    assert call(ldy=32) == INVALID
+    assert call(w_sign=MIS) == ALIGN
+    assert call(Y=0) == INVALID
+    assert call(M=0) == OK
+    assert call(M=0, Y=0, w_sign=0) == OK
+
+
 def test_binding_refuses_host_tensors():
     import torch
     from binary_ternary_matmul_amd import bwta_ternarize_pack

@@ -9,6 +9,8 @@ Every packed plane, alpha and nnz is compared in full, bit-exact.  Products:
     against 28672 x 8192 and 8192 x 28672 weights, and against gate and up
     stacked into one 57344 x 8192 weight) and both attention products are
     compared in full against the oracle;
+  * the two-plane residual product on the LLaMA-7B q and down linears: both
+    interleaved planes and scales in full, outputs on a sample;
   * the BERT-base and LLaMA-7B prefill GEMMs on a seeded sample of rows x
     columns (always including the first and last of each), accumulators and
     bf16 outputs bit-exact, and on every output through two properties any
@@ -208,3 +210,27 @@ def test_full_fused_attention(bw, oracle):
     """bwta_attention at 32 heads x 2048 x 128, fp32 out (bench's call)."""
     from tests.test_attention_gpu import check_attention
     check_attention(bw, oracle, 32, 2048, threads=THREADS, p_heads=(0, 13, 31))
+
+
+@pytest.mark.parametrize("name", ["q", "down"])
+def test_full_llama7b_residual(bw, oracle, name):
+    """Two-plane residual weights for a LLaMA-7B prefill linear (M = 2048, bf16 in
+    and out, bench's call): planes and scales in full, a sample of outputs."""
+    from tests.test_residual_gpu import expected_planes
+    acts, lins = inputs.llama7b_prefill()
+    lin = [l for l in lins if l.name == name][0]
+    x = acts[inputs.LLAMA7B_INPUTS[lin.name]]()
+    w = lin.w()
+    a = bw.bwta_ternarize_pack(to_dev(x))
+    wp = bw.bwta_pack_weights_residual(to_dev(w))
+    s1, a1, s2, a2, sign, alpha = expected_planes(oracle, w)
+    del w
+    assert (to_host(wp.sign) == sign).all()
+    assert (to_host(wp.alpha).view(np.uint32) == alpha.view(np.uint32)).all()
+    t, aa, _ = _check_planes(bw, oracle, a, x)
+    y = to_host(bw.bwta_gemm_residual(a, wp, "bf16"))
+    R, C = _sample(lin.M, 160, 300), _sample(lin.N, 96, 301)
+    acc1 = oracle.matmul_i32(t[R], s1[C], threads=THREADS)
+    acc2 = oracle.matmul_i32(t[R], s2[C], threads=THREADS)
+    ref = oracle.scale_residual(acc1, acc2, aa[R], a1[C], a2[C])
+    assert (y[np.ix_(R, C)] == oracle.to_bf16(ref)).all()
