@@ -220,6 +220,37 @@ def bench_residual(bw, pre, reps=5):
             "time_vs_one_plane": round(tot_ms / pre["gemm_ms"], 2), "per_gemm": res}
 
 
+def bench_gemv_residual(bw, copies=12, reps=3):
+    """Decode with two-plane residual weights (bwta_gemv_residual): HBM GB/s over
+    rotating copies of both planes (> 350 MB per shape)."""
+    import torch
+    from binary_ternary_matmul_amd import inputs
+    out = {}
+    for shape in ("gate_up", "down"):
+        lin16 = [l for l in inputs.llama70b_decode(16) if l.name == shape][0]
+        wr = bw.bwta_pack_weights_residual(dev(lin16.w()))
+        ws = [wr] + [bw.ResidualPlanes(wr.sign.clone(), wr.alpha.clone(), wr.K)
+                     for _ in range(copies - 1)]
+        for M in (1, 4, 16):
+            lin = [l for l in inputs.llama70b_decode(M) if l.name == shape][0]
+            a = bw.bwta_ternarize_pack(dev(lin.x()))
+            y = torch.empty((M, lin.N), dtype=torch.float32, device="cuda")
+
+            def run(a=a, y=y):
+                for w in ws:
+                    bw.bwta_gemv_residual(a, w, "f32", y)
+            us = time_calls(run, reps=reps) * 1e3 / len(ws)
+            kp = bw.padded_k(lin.K)
+            nbytes = 2 * lin.N * kp / 8 + 8 * lin.N + M * (2 * kp / 8 + 8) + 4 * M * lin.N
+            gbs = nbytes / (us * 1e-6) / 1e9
+            kern = "gemv_popcount_kernel" if M <= 4 else "gemm_mfma_kernel"  # two-plane modes
+            out[f"{shape}_M{M}"] = {"N": lin.N, "K": lin.K, "kernel": kern,
+                                    "us": round(us, 2), "bytes": int(nbytes), "GBps": round(gbs, 1),
+                                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 3)}
+        del ws, wr
+    return out
+
+
 def bench_gemv(bw, copies=24, reps=4):
     """Decode: HBM GB/s with rotating packed-weight copies (> 512 MB per shape)."""
     import torch
@@ -519,6 +550,8 @@ def main():
         line["residual"] = bench_residual(bw, pre)
         log("[bench] gemv")
         line["gemv"] = bench_gemv(bw)
+        log("[bench] gemv, two-plane residual weights")
+        line["residual"]["decode"] = bench_gemv_residual(bw)
         log("[bench] attention")
         line["attention"] = bench_attention(bw)
         log("[bench] bert")

@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
     L.bwta_pack_weights_residual.argtypes = [P, I32, I64, I64, I64, P, P, P]
     L.bwta_gemm_residual.restype = I32
     L.bwta_gemm_residual.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, I32, I64, P]
+    L.bwta_gemv_residual.restype = I32
+    L.bwta_gemv_residual.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, I32, I64, P]
     L.bwta_attention.restype = I32
     L.bwta_attention.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, ctypes.c_float, P, I32,
                                  P, P, P, P, P]
@@ -277,6 +279,17 @@ def bwta_pack_weights_residual(W: torch.Tensor) -> ResidualPlanes:
 def bwta_gemm_residual(a: TernaryPlanes, w: ResidualPlanes, out_dtype: str = "f32",
                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y[M, N] = alpha_a * (alpha1 * (t @ s1^T) + alpha2 * (t @ s2^T))."""
+    return _residual(lib().bwta_gemm_residual, "bwta_gemm_residual", a, w, out_dtype, out)
+
+
+def bwta_gemv_residual(a: TernaryPlanes, w: ResidualPlanes, out_dtype: str = "f32",
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The same product for M <= 16 activation rows (decode)."""
+    return _residual(lib().bwta_gemv_residual, "bwta_gemv_residual", a, w, out_dtype, out)
+
+
+def _residual(fn, name, a: TernaryPlanes, w: ResidualPlanes, out_dtype: str,
+              out: Optional[torch.Tensor]) -> torch.Tensor:
     if a.K != w.K:
         raise ValueError(f"K mismatch: activations {a.K}, weights {w.K}")
     M, N = a.mask.shape[0], w.sign.shape[0] // 2
@@ -284,8 +297,7 @@ def bwta_gemm_residual(a: TernaryPlanes, w: ResidualPlanes, out_dtype: str = "f3
         out = torch.empty((M, N), dtype=_OUT_TORCH[out_dtype], device=a.mask.device)
     if out.dim() != 2 or out.shape[0] != M or out.shape[1] < N or out.stride(1) != 1:
         raise ValueError("out must be [M, >=N] with unit column stride")
-    _check(lib().bwta_gemm_residual(_ptr(a.mask), _ptr(a.sign), _ptr(a.alpha), _ptr(a.nnz),
-                                    _ptr(w.sign), _ptr(w.alpha), M, N, a.K, _ptr(out),
-                                    DTYPES[out_dtype], out.stride(0), _stream()),
-           "bwta_gemm_residual")
+    _check(fn(_ptr(a.mask), _ptr(a.sign), _ptr(a.alpha), _ptr(a.nnz), _ptr(w.sign),
+              _ptr(w.alpha), M, N, a.K, _ptr(out), DTYPES[out_dtype], out.stride(0), _stream()),
+           name)
     return out

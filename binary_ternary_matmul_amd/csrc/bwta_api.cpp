@@ -242,6 +242,44 @@ bwta_status bwta_gemm_residual(const uint8_t* a_mask, const uint8_t* a_sign, con
                   "bwta_gemm_residual launch");
 }
 
+bwta_status bwta_gemv_residual(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
+                               const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha,
+                               int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype,
+                               int64_t ldy, void* stream) {
+  if (M < 0 || N < 0) return fail(BWTA_ERR_INVALID, "negative size M=%lld N=%lld", (long long)M, (long long)N);
+  BWTA_TRY(check_k(K));
+  if (!valid_io_dtype(y_dtype)) return fail(BWTA_ERR_INVALID, "bad output dtype %d", (int)y_dtype);
+  if (ldy < N) return fail(BWTA_ERR_INVALID, "ldy (%lld) < N (%lld)", (long long)ldy, (long long)N);
+  if (M > 16) return fail(BWTA_ERR_UNSUPPORTED, "bwta_gemv_residual takes M <= 16 (got %lld)", (long long)M);
+  if (N % 32 != 0)
+    return fail(BWTA_ERR_UNSUPPORTED, "N = %lld is not a multiple of 32", (long long)N);
+  if (M == 0 || N == 0) return BWTA_OK;  // empty: pointers may be NULL
+  BWTA_TRY(check_plane(a_mask, "a_mask"));
+  BWTA_TRY(check_plane(a_sign, "a_sign"));
+  BWTA_TRY(check_plane(w_sign, "w_sign"));
+  BWTA_TRY(check_word(a_alpha, true, "a_alpha"));
+  BWTA_TRY(check_word(a_nnz, true, "a_nnz"));
+  BWTA_TRY(check_word(w_alpha, true, "w_alpha"));
+  if (!Y) return fail(BWTA_ERR_INVALID, "Y is NULL");
+  if (!aligned(Y, dtype_size(y_dtype))) return fail(BWTA_ERR_ALIGN, "Y is not aligned to its element");
+  // The streaming kernel reads 16-byte words of each plane row and holds up to
+  // 4 activation rows per launch (gate/up at M = 1: 11.4 us, 5.2 TB/s; M = 4:
+  // 31 us); more rows, or rows of another length, take the two-plane GEMM
+  // kernel (≈ 40 us at M = 16; it needs K > 64).
+  const int64_t row_bytes = (K + 63) / 64 * 8;
+  if (row_bytes % 16 == 0 && M <= 4) {
+    bwta::GemmArgs g{a_mask, a_sign, a_alpha, a_nnz, 0, nullptr, w_sign, w_alpha, 0,
+                     1, M, N, K, Y, elt(y_dtype), ldy, 0};
+    return from_hip(bwta::launch_gemv_popcount_residual(g, static_cast<hipStream_t>(stream)),
+                    "bwta_gemv_residual launch");
+  }
+  if (K <= 64) return fail(BWTA_ERR_UNSUPPORTED, "K = %lld (two-plane product needs K > 64)", (long long)K);
+  bwta::GemmArgs g{a_mask, a_sign, a_alpha, a_nnz, 0, nullptr, w_sign, w_alpha, 0,
+                   1, M, 2 * N, K, Y, elt(y_dtype), ldy, 0};
+  return from_hip(bwta::launch_gemm_mfma_residual(g, static_cast<hipStream_t>(stream)),
+                  "bwta_gemv_residual launch");
+}
+
 bwta_status bwta_gemv(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
                       const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha, int64_t M,
                       int64_t N, int64_t K, void* Y, bwta_dtype y_dtype, int64_t ldy,

@@ -178,7 +178,12 @@ __device__ __forceinline__ int bitrev(int x) {
   return r;
 }
 
-template <int MB, int NCH, int R, int OUT>
+// RES: two-plane residual weights, planes interleaved in groups of 32 rows; N
+// counts outputs.  A wave takes two adjacent outputs o, o + 1 (o even) and
+// their four plane rows b, b + 1 (plane 1) and b + 32, b + 33 (plane 2),
+// b = 64 (o / 32) + o % 32, and each output lane fetches its plane-2 count from
+// the lane that holds it: y = acc1 * (alpha_a * alpha1) + acc2 * (alpha_a * alpha2).
+template <int MB, int NCH, int R, int OUT, bool RES = false>
 __global__ void __launch_bounds__(256)
 gemv_popcount_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__ a_sign,
                      const float* __restrict__ a_alpha, const int32_t* __restrict__ a_nnz,
@@ -219,16 +224,19 @@ gemv_popcount_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restri
     sa[m] = OUT == (int)Elt::I32 ? 0.0f : a_alpha[row];
   }
 
-  for (int64_t n0 = wave * R; n0 < N; n0 += nwaves * R) {
+  static_assert(!RES || (R == 4 && OUT != (int)Elt::I32), "two-plane rows come in fours");
+  constexpr int STEP = RES ? 2 : R;  // outputs per wave iteration
+  for (int64_t n0 = wave * STEP; n0 < N; n0 += nwaves * STEP) {
     int cnt[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) cnt[i] = 0;
+    const int64_t pbase = 64 * (n0 >> 5) + (n0 & 31);  // RES: plane row of output n0
     u32x4 w[R][NCH];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const int64_t n = n0 + r < N ? n0 + r : N - 1;
+        const int64_t n = RES ? pbase + (r & 1) + (r >> 1) * 32 : (n0 + r < N ? n0 + r : N - 1);
         w[r][c] = cvalid[c] ? load_nt16(w_sign + n * row_bytes + (int64_t)c * 1024 + lane * 16)
                             : u32x4{0, 0, 0, 0};
       }
@@ -244,6 +252,29 @@ gemv_popcount_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restri
             cnt[r * MB + m] += __builtin_popcount((ww[q] & ap[m][c][q]) | (~ww[q] & as[m][c][q]));
       }
     wave_reduce_scatter_int<V>(cnt);
+    if constexpr (RES) {
+      const int v = bitrev<LOGV>(lane & (V - 1));
+      const int other = __shfl(cnt[0], bitrev<LOGV>(v ^ (2 * MB)), kWave);  // plane 2
+      const int r = v / MB, m = v - r * MB;
+      if (lane < V && r < 2 && m < m_count) {
+        float sam = sa[0];
+#pragma unroll
+        for (int mm = 1; mm < MB; ++mm) sam = m == mm ? sa[mm] : sam;
+        int nzm = nz[0];
+#pragma unroll
+        for (int mm = 1; mm < MB; ++mm) nzm = m == mm ? nz[mm] : nzm;
+        const float a1 = w_alpha[pbase + r], a2 = w_alpha[pbase + r + 32];
+        const float y1 = (float)(nzm - 2 * cnt[0]) * (sam * a1);
+        const float y2 = (float)(nzm - 2 * other) * (sam * a2);
+        const float y = y1 + y2;
+        const int64_t idx = (int64_t)(m_base + m) * ldy + n0 + r;
+        if constexpr (OUT == (int)Elt::F32)
+          reinterpret_cast<float*>(Y)[idx] = y;
+        else
+          reinterpret_cast<uint16_t*>(Y)[idx] = f32_to_bf16_rne(y);
+      }
+      continue;
+    }
     if (lane < V) {
       const int v = bitrev<LOGV>(lane);
       const int r = v / MB, m = v - r * MB;
@@ -279,23 +310,23 @@ hipError_t launch_gemm_pc_out(const GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MB, int NCH, int OUT>
+template <int MB, int NCH, int OUT, bool RES = false>
 hipError_t launch_gemv_cfg(const GemmArgs& g, int m_base, int m_count, hipStream_t stream) {
   // Four weight rows per wave (4 KiB of loads per 1 KiB chunk column): for
   // M = 1 this streams faster than 1, 2, 8 or 16 rows per wave.
   constexpr int R = 4;
   const int64_t row_bytes = (g.K + 63) / 64 * 8;
-  const int64_t waves_needed = (g.N + R - 1) / R;
+  const int64_t waves_needed = (g.N + (RES ? 2 : R) - 1) / (RES ? 2 : R);
   int64_t blocks = (waves_needed + 3) / 4;
   const int64_t cap = 256 * 8;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL((gemv_popcount_kernel<MB, NCH, R, OUT>), dim3((unsigned)blocks), dim3(256), 0,
+  hipLaunchKernelGGL((gemv_popcount_kernel<MB, NCH, R, OUT, RES>), dim3((unsigned)blocks), dim3(256), 0,
                      stream, g.a_mask, g.a_sign, g.a_alpha, g.a_nnz, m_base, m_count, g.b_sign,
                      g.b_alpha, g.N, row_bytes, g.Y, g.ldy);
   return hipGetLastError();
 }
 
-template <int NCH, int OUT>
+template <int NCH, int OUT, bool RES = false>
 hipError_t launch_gemv_nch(const GemmArgs& g, hipStream_t stream) {
   // activation registers: 8 * MB * NCH <= 128
   constexpr int MBMAX = 16 / NCH >= 4 ? 4 : (16 / NCH >= 2 ? 2 : 1);
@@ -303,24 +334,24 @@ hipError_t launch_gemv_nch(const GemmArgs& g, hipStream_t stream) {
     const int cnt = (int)(g.M - m0 < MBMAX ? g.M - m0 : MBMAX);
     hipError_t e;
     if (cnt == 1)
-      e = launch_gemv_cfg<1, NCH, OUT>(g, (int)m0, 1, stream);
+      e = launch_gemv_cfg<1, NCH, OUT, RES>(g, (int)m0, 1, stream);
     else if (cnt == 2 || MBMAX == 2)
-      e = launch_gemv_cfg<(MBMAX >= 2 ? 2 : 1), NCH, OUT>(g, (int)m0, cnt, stream);
+      e = launch_gemv_cfg<(MBMAX >= 2 ? 2 : 1), NCH, OUT, RES>(g, (int)m0, cnt, stream);
     else
-      e = launch_gemv_cfg<MBMAX, NCH, OUT>(g, (int)m0, cnt, stream);
+      e = launch_gemv_cfg<MBMAX, NCH, OUT, RES>(g, (int)m0, cnt, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-template <int OUT>
+template <int OUT, bool RES = false>
 hipError_t launch_gemv_out(const GemmArgs& g, hipStream_t stream) {
   const int64_t row_bytes = (g.K + 63) / 64 * 8;
   const int64_t nch = (row_bytes + 1023) / 1024;
-  if (nch <= 1) return launch_gemv_nch<1, OUT>(g, stream);
-  if (nch <= 2) return launch_gemv_nch<2, OUT>(g, stream);
-  if (nch <= 4) return launch_gemv_nch<4, OUT>(g, stream);
-  if (nch <= 8) return launch_gemv_nch<8, OUT>(g, stream);
+  if (nch <= 1) return launch_gemv_nch<1, OUT, RES>(g, stream);
+  if (nch <= 2) return launch_gemv_nch<2, OUT, RES>(g, stream);
+  if (nch <= 4) return launch_gemv_nch<4, OUT, RES>(g, stream);
+  if (nch <= 8) return launch_gemv_nch<8, OUT, RES>(g, stream);
   return hipErrorInvalidValue;
 }
 
@@ -342,6 +373,17 @@ hipError_t launch_gemv_popcount(const GemmArgs& g, hipStream_t stream) {
     case Elt::I32: return launch_gemv_out<(int)Elt::I32>(g, stream);
   }
   return hipErrorInvalidValue;
+}
+
+// Two-plane residual weights, M <= 16: g.N counts outputs (a multiple of 32),
+// g.b_sign / g.b_alpha hold 2 g.N interleaved plane rows.
+hipError_t launch_gemv_popcount_residual(const GemmArgs& g, hipStream_t stream) {
+  if (g.N % 32 != 0) return hipErrorInvalidValue;
+  switch (g.y_dt) {
+    case Elt::F32: return launch_gemv_out<(int)Elt::F32, true>(g, stream);
+    case Elt::BF16: return launch_gemv_out<(int)Elt::BF16, true>(g, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace bwta

@@ -167,6 +167,17 @@ bwta_status bwta_gemm_residual(const uint8_t* a_mask, const uint8_t* a_sign, con
                                int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype,
                                int64_t ldy, void* stream);
 
+/* Decode with two-plane residual weights, 1 <= M <= 16: the product of
+ * bwta_gemm_residual; for M <= 4 and row_bytes(K) a multiple of 16 by a kernel
+ * that streams both planes from HBM once (each wave reads the four plane rows
+ * of two adjacent outputs), otherwise by bwta_gemm_residual's kernel.
+ * N a multiple of 32, M <= 16, and K > 64 unless that streaming kernel applies
+ * (else BWTA_ERR_UNSUPPORTED); a_nnz is required. */
+bwta_status bwta_gemv_residual(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
+                               const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha,
+                               int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype,
+                               int64_t ldy, void* stream);
+
 /* Decode GEMV / skinny GEMM, 1 <= M <= 16: the same product as bwta_gemm with
  * kernels that stream the packed weights from HBM once (page: Abstract, lower
  * memory footprint; the replies quoted on the page name prefill and decode as

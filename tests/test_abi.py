@@ -182,6 +182,15 @@ def test_residual_validation(L):
     assert call(Y=0) == INVALID
     assert call(M=0) == OK
     assert call(M=0, Y=0, w_sign=0) == OK
+    v = L.bwta_gemv_residual
+
+    def callv(M=4, N=64, K=128, Y=A, dt=0, ldy=64, a_nnz=A):
+        return v(P(A), P(A), P(A), P(a_nnz), P(A), P(A), M, N, K, P(Y), dt, ldy, P(0))
+    assert callv(M=17) == UNSUPPORTED
+    assert callv(N=40) == UNSUPPORTED
+    assert callv(a_nnz=0) == INVALID                                   # the decode path needs nnz
+    assert callv(dt=2) == INVALID
+    assert callv(M=0, Y=0) == OK
 
 
 def test_binding_refuses_host_tensors():

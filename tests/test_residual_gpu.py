@@ -114,3 +114,33 @@ def test_gemm_residual_rejects_k64(bw):
     wp = bw.bwta_pack_weights_residual(to_dev(w))
     with pytest.raises(bw.BwtaError):
         bw.bwta_gemm_residual(a, wp, "f32")
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(1, 32, 128), (1, 64, 100), (3, 96, 100), (4, 128, 8192),
+                                   (7, 64, 2000), (16, 160, 4100), (16, 32, 28672),
+                                   (2, 64, 129)])
+def test_gemv_residual(bw, oracle, M, N, K, out_dtype):
+    """Decode with two-plane weights: every output bit-exact.  M > 4, and K = 4100
+    and 129 (plane rows not a multiple of 16 bytes), take the two-plane GEMM
+    kernel; the rest the streaming kernel."""
+    x, w = inputs.random_linear(M * 5 + N + K, M, K, N)
+    a = bw.bwta_ternarize_pack(to_dev(x))
+    wp = bw.bwta_pack_weights_residual(to_dev(w))
+    y = to_host(bw.bwta_gemv_residual(a, wp, out_dtype))
+    t, aa, _ = oracle.ternarize(x)
+    s1, a1, s2, a2 = oracle.binarize_residual(w)
+    ref = oracle.scale_residual(oracle.matmul_i32(t, s1), oracle.matmul_i32(t, s2), aa, a1, a2)
+    if out_dtype == "bf16":
+        assert (y == oracle.to_bf16(ref)).all()
+    else:
+        assert (y.view(np.uint32) == ref.view(np.uint32)).all()
+
+
+def test_gemv_residual_rejects_short_rows(bw):
+    """Plane rows of one 8-byte word (K <= 64) are not offered."""
+    x, w = inputs.random_linear(11, 1, 64, 32)
+    a = bw.bwta_ternarize_pack(to_dev(x))
+    wp = bw.bwta_pack_weights_residual(to_dev(w))
+    with pytest.raises(bw.BwtaError):
+        bw.bwta_gemv_residual(a, wp, "f32")
