@@ -163,7 +163,8 @@ attention_kernel(const uint8_t* __restrict__ q_mask, const uint8_t* __restrict__
   // P rows padded by 16 bytes so that the 16 rows read together hit different banks
   __shared__ __attribute__((aligned(16))) uint32_t plane[kRows][RB / 4 + 4];
 
-  // The head's K planes, staged once: mask at slot kslot(j), sign kSlots(L) on.
+  // The head's K planes, staged once as q01 words at slot kslot(j) and q23
+  // words kSlots(L) slots on.
   extern __shared__ __attribute__((aligned(16))) uint8_t kbuf[];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -181,11 +182,20 @@ attention_kernel(const uint8_t* __restrict__ q_mask, const uint8_t* __restrict__
       km[i] = *reinterpret_cast<const v4u*>(k_mask + (h * L + j) * 16);
       ks[i] = *reinterpret_cast<const v4u*>(k_sign + (h * L + j) * 16);
     }
+    // Staged as q01 = (mask bits 4j, 4j+1 | sign bits of the same k, shifted 2)
+    // and q23 (the same for 4j+2, 4j+3): slice e of a word is then one mask (odd
+    // e) or a shift and a mask (even e) of q01 or q23, as in ternary_slice.
 #pragma unroll
     for (int i = 0; i < L / (W * kWave); ++i) {
       const int j = kslot(i * W * kWave + threadIdx.x);
-      *reinterpret_cast<v4u*>(kbuf + j * 16) = km[i];
-      *reinterpret_cast<v4u*>(kbuf + (kSlots(L) + j) * 16) = ks[i];
+      v4u q01, q23;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        q01[x] = (km[i][x] & 0x33333333u) | ((ks[i][x] << 2) & 0xCCCCCCCCu);
+        q23[x] = ((km[i][x] >> 2) & 0x33333333u) | (ks[i][x] & 0xCCCCCCCCu);
+      }
+      *reinterpret_cast<v4u*>(kbuf + j * 16) = q01;
+      *reinterpret_cast<v4u*>(kbuf + (kSlots(L) + j) * 16) = q23;
     }
   }
   lds_barrier();
@@ -215,13 +225,15 @@ attention_kernel(const uint8_t* __restrict__ q_mask, const uint8_t* __restrict__
   }
   const v4f aq = *reinterpret_cast<const v4f*>(q_alpha + q0 + 4 * g);
   float u[T][4];  // u = S * alpha_k, rows 4g + r of the block, key kk + t
+  // lane group g reads q01 (g < 2) or q23 and shifts by 1 for even g
+  const uint8_t* kq = kbuf + ((g >> 1) * kSlots(L) + kslot(j0)) * 16;
+  const uint32_t ksh = 1u - (uint32_t)(g & 1);
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const v4u m = *reinterpret_cast<const v4u*>(kbuf + (kslot(j0) + t) * 16);
-    const v4u s = *reinterpret_cast<const v4u*>(kbuf + (kSlots(L) + kslot(j0) + t) * 16);
+    const v4u q = *reinterpret_cast<const v4u*>(kq + t * 16);
     v4i b;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) b[x] = (int)ternary_slice(m[x], s[x], g);
+    for (int x = 0; x < 4; ++x) b[x] = (int)((q[x] << ksh) & 0xAAAAAAAAu);
     const v4f acc = mfma_fp4(a, b, v4f{0.f, 0.f, 0.f, 0.f}, 127);
 #pragma unroll
     for (int r = 0; r < 4; ++r) u[t][r] = acc[r] * ak[t];
