@@ -270,18 +270,21 @@ attention_kernel(const uint8_t* __restrict__ q_mask, const uint8_t* __restrict__
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = 4 * g + r;
-    float m = red[0][0][row];
-#pragma unroll
-    for (int i = 1; i < W; ++i) m = fmaxf(m, red[0][i][row]);
+    // Lane c takes wave c % W: the row maximum, then f and s f of that wave, and
+    // the pairwise tree over the W waves in order (lane bits 0, 1, then the
+    // half-row mirror, which pairs lane quads 0-3 and 4-7).
+    const float mi = red[0][c & (W - 1)][row];
+    float m = fmaxf(mi, dppf<kXor1>(mi));
+    if constexpr (W > 2) m = fmaxf(m, dppf<kXor2>(m));
+    if constexpr (W > 4) m = fmaxf(m, dppf<kHalfMirror>(m));
     const float off = -(coef[r] * m);
-    float f[W], sw[W];
-#pragma unroll
-    for (int i = 0; i < W; ++i) {
-      f[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(coef[r], red[0][i][row], off));
-      sw[i] = red[1][i][row] * f[i];
-    }
+    float sw = red[1][c & (W - 1)][row] *
+               __builtin_amdgcn_exp2f(__builtin_fmaf(coef[r], mi, off));
+    sw = sw + dppf<kXor1>(sw);
+    if constexpr (W > 2) sw = sw + dppf<kXor2>(sw);
+    if constexpr (W > 4) sw = sw + dppf<kHalfMirror>(sw);
     const float fw = __builtin_amdgcn_exp2f(__builtin_fmaf(coef[r], red[0][w][row], off));
-    const float k = fw / lane_tree<W>(sw);
+    const float k = fw / sw;
     float pr[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) pr[t] = u[t][r] = u[t][r] * k;
