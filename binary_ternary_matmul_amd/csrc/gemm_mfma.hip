@@ -728,7 +728,12 @@ hipError_t launch_b(const GemmArgs& g, hipStream_t stream) {
   const int64_t tm = (g.M + WAVE_TILE - 1) / WAVE_TILE;
   const int64_t tn = (g.N + WAVE_TILE - 1) / WAVE_TILE;
   const int64_t steps = (row_bytes / 8 + 3) / 4;
-  const int S = choose_split(tm * tn * g.batch, steps);
+  // From 1024 tiles on (a full round of single-wave tiles) splitting K only
+  // adds exchange work: LLaMA-7B gate/up (1376 tiles) 80 us unsplit, 84 / 118 us
+  // with S = 2 / 4; below that the split fills the idle SIMDs (q, o, down:
+  // 512 tiles, 30.5 us with S = 2 against 36.6 unsplit).
+  const int64_t tiles = tm * tn * g.batch;
+  const int S = tiles >= 1024 ? 1 : choose_split(tiles, steps);
   switch (g.y_dt) {
     case Elt::F32:
       return launch_s<B_TERNARY, (int)Elt::F32>(g, S, row_bytes, tm, tn, stream);
@@ -754,9 +759,8 @@ hipError_t launch_gemm_mfma_residual(const GemmArgs& g, hipStream_t stream) {
   const int64_t tm = (g.M + WAVE_TILE - 1) / WAVE_TILE;
   const int64_t tn = (g.N + WAVE_TILE - 1) / WAVE_TILE;
   const int64_t steps = (row_bytes / 8 + 3) / 4;
-  // Twice the tiles of the one-plane product: from 1024 tiles on, splitting K
-  // only adds exchange work (LLaMA-7B gate: 125 us unsplit, 163 / 225 us with
-  // S = 2 / 4).
+  // As for one plane (two-plane LLaMA-7B gate: 125 us unsplit, 163 / 225 us
+  // with S = 2 / 4).
   const int64_t tiles = tm * tn * g.batch;
   const int S = tiles >= 1024 ? 1 : choose_split(tiles, steps);
   return g.y_dt == Elt::F32
