@@ -19,7 +19,8 @@
 // Design (head dim 128, L = 256 W keys per head, W in {2, 4, 8}):
 // * One block = 64 query rows of one head in 4 passes of 16, W waves.  The
 //   head's K planes (32 bytes per key) are staged in LDS once per block with
-//   coalesced loads, so each K byte leaves L2 once per 64 query rows.
+//   coalesced loads, already merged into the slice scheme's q01/q23 words, so
+//   each K byte leaves L2 once per 64 query rows.
 // * In a pass, wave w owns the keys [256 w, 256 (w+1)).  Its score tile t
 //   (t < 16) holds, in MFMA column c, key 256 w + 16 c + t, so the 16 scores a
 //   lane holds per row are consecutive keys: the first four levels of the
@@ -32,7 +33,10 @@
 //   as +-1.0 = 0x2 / 0xA or 0), a permutation of d that A and B share, so the
 //   instruction sums t_q[d] t_k[d] over all 128 d exactly.
 // * Softmax: u = S * alpha_k[j] per score; with a = alpha_q * scale * log2(e)
-//   per row, e = exp2(a u - a max u) (one fma and v_exp_f32), p = e * (1 / sum e).
+//   per row, each wave takes e = exp2(a u - a m_w) against its own maximum m_w
+//   (one fma and v_exp_f32) and its sum s_w; one LDS exchange gives the row
+//   maximum m and s = sum_w s_w f_w, f_w = exp2(a m_w - a m), and
+//   p = e * (f_w / s).
 // * P V on the same instruction with the decode kernel's scheme: V^T bits are
 //   the A operand (b * {0.5, 1, 2, 2} in slices e = 0..3, brought to b by the
 //   A scale 2^{1, 0, -1, -1}), P's mask bits (kept from LDS) the B operand as
