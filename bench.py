@@ -243,7 +243,7 @@ def bench_gemv_residual(bw, copies=12, reps=3):
             kp = bw.padded_k(lin.K)
             nbytes = 2 * lin.N * kp / 8 + 8 * lin.N + M * (2 * kp / 8 + 8) + 4 * M * lin.N
             gbs = nbytes / (us * 1e-6) / 1e9
-            kern = "gemv_popcount_kernel" if M <= 4 else "gemm_mfma_kernel"  # two-plane modes
+            kern = "gemv_popcount_kernel" if M == 1 else "gemv_mfma_kernel"  # two-plane modes
             out[f"{shape}_M{M}"] = {"N": lin.N, "K": lin.K, "kernel": kern,
                                     "us": round(us, 2), "bytes": int(nbytes), "GBps": round(gbs, 1),
                                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 3)}

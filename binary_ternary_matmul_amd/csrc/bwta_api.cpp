@@ -263,22 +263,16 @@ bwta_status bwta_gemv_residual(const uint8_t* a_mask, const uint8_t* a_sign, con
   BWTA_TRY(check_word(w_alpha, true, "w_alpha"));
   if (!Y) return fail(BWTA_ERR_INVALID, "Y is NULL");
   if (!aligned(Y, dtype_size(y_dtype))) return fail(BWTA_ERR_ALIGN, "Y is not aligned to its element");
-  // The streaming kernel reads 16-byte words of each plane row and holds up to
-  // 4 activation rows per launch (gate/up at M = 1: 11.4 us, 5.2 TB/s; M = 4:
-  // 31 us); more rows, or rows of another length, take the two-plane GEMM
-  // kernel (≈ 40 us at M = 16; it needs K > 64).
+  // One activation row: the popcount GEMV (16-byte words of each plane row;
+  // 70B gate/up 11.4 us, 5.2 TB/s); more rows or other row lengths: the FP4
+  // GEMV, whose cost does not grow with M.
   const int64_t row_bytes = (K + 63) / 64 * 8;
-  if (row_bytes % 16 == 0 && M <= 4) {
-    bwta::GemmArgs g{a_mask, a_sign, a_alpha, a_nnz, 0, nullptr, w_sign, w_alpha, 0,
-                     1, M, N, K, Y, elt(y_dtype), ldy, 0};
-    return from_hip(bwta::launch_gemv_popcount_residual(g, static_cast<hipStream_t>(stream)),
-                    "bwta_gemv_residual launch");
-  }
-  if (K <= 64) return fail(BWTA_ERR_UNSUPPORTED, "K = %lld (two-plane product needs K > 64)", (long long)K);
   bwta::GemmArgs g{a_mask, a_sign, a_alpha, a_nnz, 0, nullptr, w_sign, w_alpha, 0,
-                   1, M, 2 * N, K, Y, elt(y_dtype), ldy, 0};
-  return from_hip(bwta::launch_gemm_mfma_residual(g, static_cast<hipStream_t>(stream)),
-                  "bwta_gemv_residual launch");
+                   1, M, N, K, Y, elt(y_dtype), ldy, 0};
+  const hipError_t e = row_bytes % 16 == 0 && M == 1
+                           ? bwta::launch_gemv_popcount_residual(g, static_cast<hipStream_t>(stream))
+                           : bwta::launch_gemv_mfma_residual(g, static_cast<hipStream_t>(stream));
+  return from_hip(e, "bwta_gemv_residual launch");
 }
 
 bwta_status bwta_gemv(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,

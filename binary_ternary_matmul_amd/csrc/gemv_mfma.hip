@@ -27,7 +27,7 @@
 //   popc(mask) - 2 popc(sign) over the row, counted while staging.
 // * Every wave owns one tile of 16 weight rows and one of S contiguous K ranges,
 //   and walks its range in order (per load instruction: 16 rows x 64 contiguous
-//   bytes).  It keeps kRing chunks of weight loads in flight from its first
+//   bytes).  It keeps kPF * kNB chunks of weight loads in flight from its first
 //   instruction on: the whole range when it is short, a ring refilled as chunks
 //   are consumed otherwise.  Ring slots past the range load from an offset the
 //   buffer range check rejects, which returns zeros without touching memory, and
@@ -60,7 +60,6 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 constexpr int kMaxW = 8;                // waves per block
 constexpr int kPF = 4;                  // chunks per batch
 constexpr int kNB = 2;                  // batches in flight
-constexpr int kRing = kPF * kNB;        // chunks in flight per wave
 constexpr int kMaxSU = 8;               // staged 16-byte units per thread and plane
 constexpr uint32_t kOOB = 0x80000000u;  // an offset past every range check
 constexpr size_t kMaxLds = 150 * 1024;
@@ -124,17 +123,24 @@ struct LdsLayout {
   uint32_t plane, zero_off, t_off, x_off, total;
 };
 
-__host__ __device__ inline LdsLayout lds_layout(bool expanded, int chunks, int M, int S, int R) {
+__host__ __device__ inline LdsLayout lds_layout(bool expanded, int chunks, int M, int S, int R,
+                                                int accs = 1) {
   LdsLayout l;
   l.plane = (uint32_t)chunks * 4u * (uint32_t)M * 16u;
   l.zero_off = 2 * l.plane;
   l.t_off = expanded ? (uint32_t)(chunks + 1) * 4096u : l.zero_off + 32u;
   l.x_off = l.t_off + kMaxW * 16u * 4u;
-  l.total = l.x_off + (S > 1 ? (uint32_t)(S * R) * 64u * 16u : 0u);
+  l.total = l.x_off + (S > 1 ? (uint32_t)(S * R * accs) * 64u * 16u : 0u);
   return l;
 }
 
-template <int S, bool X, int OUT>
+// RES: two-plane residual weights (planes interleaved in groups of 32 rows), N
+// counts outputs.  The wave of output tile o (16 outputs) streams both of its
+// plane tiles - rows 64 (o / 2) + 16 (o % 2) and 32 rows further - with half as
+// many chunks per batch (the same bytes in flight), multiplies both by the same
+// activation operands, and the epilogue writes
+// y = (T - 2 U1) (alpha_a alpha1) + (T - 2 U2) (alpha_a alpha2).
+template <int S, bool X, int OUT, bool RES = false>
 __global__ void __launch_bounds__(kMaxW * kWave)
 gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__ a_sign,
                  const float* __restrict__ a_alpha, int M, const uint8_t* __restrict__ w_sign,
@@ -148,13 +154,18 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   const int rg = wid / S, ks = wid - rg * S;
   const int r = lane & 15;
   const int g = lane >> 4;
-  const int64_t n0 = ((int64_t)blockIdx.x * R + rg) * 16;
+  static_assert(!RES || OUT != (int)Elt::I32, "two-plane products are scaled");
+  constexpr int PF = RES ? kPF / 2 : kPF;  // chunks per batch and plane
+  constexpr int RING = PF * kNB;
+  const int64_t ot = (int64_t)blockIdx.x * R + rg;  // output tile
+  const int64_t n0 = ot * 16;
+  const int64_t p1 = RES ? 64 * (ot >> 1) + 16 * (ot & 1) : n0;  // its (first) plane rows
   const int64_t rows_left = N - n0;
   const int rows_here = rows_left <= 0 ? 0 : (rows_left < 16 ? (int)rows_left : 16);
   const int chunks = (row_bytes + 63) / 64;
   const int c0 = chunks * ks / S;
   const int c1 = chunks * (ks + 1) / S;
-  const LdsLayout L = lds_layout(X, chunks, M, S, R);
+  const LdsLayout L = lds_layout(X, chunks, M, S, R, RES ? 2 : 1);
   int* tsum = reinterpret_cast<int*>(smem + L.t_off);
 
   // 1. Epilogue scales.  Items: S = 1, the lanes of the own wave; S > 1, item
@@ -164,14 +175,19 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   const bool item_ok = S == 1 || p_item < R * kWave;
   const int64_t nb_item = S == 1 ? n0 : ((int64_t)blockIdx.x * R + p_item / kWave) * 16;
   const int l_item = p_item % kWave;
-  v4f ab = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  v4f ab = v4f{0.0f, 0.0f, 0.0f, 0.0f}, ab2 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   float aa = 0.0f;
   if constexpr (OUT != (int)Elt::I32) {
-    const __amdgpu_buffer_rsrc_t ars = checked_rsrc(w_alpha, (uint32_t)(N * 4));
+    const __amdgpu_buffer_rsrc_t ars = checked_rsrc(w_alpha, (uint32_t)((RES ? 2 : 1) * N * 4));
     const int64_t n = nb_item + 4 * (l_item >> 4);
+    // plane row of output n (RES: interleaved groups of 32)
+    const int64_t pn = RES ? 64 * (n >> 5) + (n & 31) : n;
     // n is a multiple of 4; the 4-byte range check zeroes the floats past N.
     ab = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
-                                     ars, (int)(n < N ? (uint32_t)(n * 4) : kOOB), 0, 0));
+                                     ars, (int)(n < N ? (uint32_t)(pn * 4) : kOOB), 0, 0));
+    if constexpr (RES)
+      ab2 = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                        ars, (int)(n < N ? (uint32_t)((pn + 32) * 4) : kOOB), 0, 0));
     const __amdgpu_buffer_rsrc_t aars = checked_rsrc(a_alpha, (uint32_t)M * 4u);
     aa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                        aars, (int)((l_item & 15) * 4), 0, 0));
@@ -215,15 +231,18 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   //    staged: a wave that queues many loads stalls on issue until the memory
   //    pipeline drains, and it has to get to the staging first.
   const __amdgpu_buffer_rsrc_t wrs =
-      checked_rsrc(w_sign + (rows_here ? n0 * row_bytes : 0), (uint32_t)(rows_here * row_bytes));
+      checked_rsrc(w_sign + (rows_here ? p1 * row_bytes : 0), (uint32_t)(rows_here * row_bytes));
+  const __amdgpu_buffer_rsrc_t wrs2 = checked_rsrc(
+      w_sign + (RES && rows_here ? (p1 + 32) * row_bytes : 0), (uint32_t)(rows_here * row_bytes));
   const uint32_t w_lane = (uint32_t)(r * row_bytes + 16 * g);
-  v4u wr[kNB][kPF];
+  v4u wr[kNB][PF], wr2[kNB][PF];
   auto issue = [&](int b, int cb) {
 #pragma unroll
-    for (int i = 0; i < kPF; ++i) {
+    for (int i = 0; i < PF; ++i) {
       const int c = cb + i;
-      wr[b][i] = __builtin_amdgcn_raw_buffer_load_b128(
-          wrs, (int)(c < c1 ? w_lane + 64u * (uint32_t)c : kOOB), 0, 0);
+      const int off = (int)(c < c1 ? w_lane + 64u * (uint32_t)c : kOOB);
+      wr[b][i] = __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0);
+      if constexpr (RES) wr2[b][i] = __builtin_amdgcn_raw_buffer_load_b128(wrs2, off, 0, 0);
     }
   };
   issue(0, c0);
@@ -294,7 +313,7 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
       *reinterpret_cast<v4u*>(smem + L.zero_off + 16 * threadIdx.x) = v4u{0u, 0u, 0u, 0u};
   }
 #pragma unroll
-  for (int b = 1; b < kNB; ++b) issue(b, c0 + b * kPF);
+  for (int b = 1; b < kNB; ++b) issue(b, c0 + b * PF);
   __builtin_amdgcn_sched_barrier(0);
   lds_barrier();
 
@@ -304,10 +323,10 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   const uint32_t am_base = X ? 0u : live ? (uint32_t)(g * M + r) * 16u : L.zero_off;
   const uint32_t as_base = live ? L.plane + am_base : L.zero_off;
   const uint32_t a_step = X ? 0u : live ? (uint32_t)(4 * M) * 16u : 0u;
-  v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f}, acc2 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   auto compute = [&](int b, int cb) {
 #pragma unroll
-    for (int i = 0; i < kPF; ++i) {
+    for (int i = 0; i < PF; ++i) {
       const int c = cb + i;
       if (c < c1) {  // uniform
         const uint32_t ao = am_base + (uint32_t)c * a_step;
@@ -335,26 +354,33 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
         acc = mfma16(weight_slice<1>(w), bop[1], acc, weight_scale(1));
         acc = mfma16(weight_slice<2>(w), bop[2], acc, weight_scale(2));
         acc = mfma16(weight_slice<3>(w), bop[3], acc, weight_scale(3));
+        if constexpr (RES) {
+          const v4u w2 = wr2[b][i];
+          acc2 = mfma16(weight_slice<0>(w2), bop[0], acc2, weight_scale(0));
+          acc2 = mfma16(weight_slice<1>(w2), bop[1], acc2, weight_scale(1));
+          acc2 = mfma16(weight_slice<2>(w2), bop[2], acc2, weight_scale(2));
+          acc2 = mfma16(weight_slice<3>(w2), bop[3], acc2, weight_scale(3));
+        }
       }
     }
   };
   // Full revolutions refill their slots; the last one issues nothing, so the
   // epilogue does not wait behind loads of chunks past the range.
   int cb = c0;
-  for (; cb + kRing < c1; cb += kRing) {
+  for (; cb + RING < c1; cb += RING) {
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
-      compute(b, cb + b * kPF);
-      issue(b, cb + b * kPF + kRing);
+      compute(b, cb + b * PF);
+      issue(b, cb + b * PF + RING);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
-  for (int b = 0; b < kNB; ++b) compute(b, cb + b * kPF);
+  for (int b = 0; b < kNB; ++b) compute(b, cb + b * PF);
 
   // 6. Epilogue.  Element u of the U tile in lane l: activation row m = l % 16,
   //    column n_base + 4 (l / 16) + u; the product is T[m] - 2U.
-  auto store = [&](int l, v4f u4, int64_t nb) {
+  auto store = [&](int l, v4f u4, v4f u4b, int64_t nb) {
     const int m = l & 15;
     const int64_t n = nb + 4 * (l >> 4);
     if (m >= M || n >= N) return;
@@ -368,7 +394,11 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
       if constexpr (OUT == (int)Elt::I32) {
         o[u] = (uint32_t)(int)accf;
       } else {
-        const float y = accf * (aa * ab[u]);
+        float y = accf * (aa * ab[u]);
+        if constexpr (RES) {
+          const float y2 = (t - 2.0f * u4b[u]) * (aa * ab2[u]);
+          y = y + y2;
+        }
         o[u] = OUT == (int)Elt::F32 ? __float_as_uint(y)
                                     : (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y);
       }
@@ -392,17 +422,24 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   };
 
   if constexpr (S == 1) {
-    if (rows_here > 0) store(lane, acc, n0);
+    if (rows_here > 0) store(lane, acc, acc2, n0);
   } else {
-    // Cross-wave sum of the S partial tiles of each row group.
+    // Cross-wave sum of the S partial tiles of each row group (and plane).
     v4f* xbuf = reinterpret_cast<v4f*>(smem + L.x_off);
+    v4f* xbuf2 = xbuf + S * R * kWave;
     xbuf[wid * kWave + lane] = acc;
+    if constexpr (RES) xbuf2[wid * kWave + lane] = acc2;
     lds_barrier();
     if (item_ok) {
       const int grp = p_item / kWave;
       v4f sum = xbuf[(grp * S) * kWave + l_item];
       for (int k2 = 1; k2 < S; ++k2) sum += xbuf[(grp * S + k2) * kWave + l_item];
-      store(l_item, sum, nb_item);
+      v4f sum2 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (RES) {
+        sum2 = xbuf2[(grp * S) * kWave + l_item];
+        for (int k2 = 1; k2 < S; ++k2) sum2 += xbuf2[(grp * S + k2) * kWave + l_item];
+      }
+      store(l_item, sum, sum2, nb_item);
     }
   }
 }
@@ -416,7 +453,7 @@ struct Geometry {
   bool fits;
 };
 
-Geometry geometry(int64_t N, int64_t row_bytes, int64_t mg) {
+Geometry geometry(int64_t N, int64_t row_bytes, int64_t mg, int accs = 1) {
   Geometry q;
   const int64_t chunks = (row_bytes + 63) / 64;
   const int64_t tiles = (N + 15) / 16;
@@ -429,16 +466,16 @@ Geometry geometry(int64_t N, int64_t row_bytes, int64_t mg) {
   if (R > kMaxW / q.S) R = kMaxW / q.S;
   q.R = (int)R;
   q.blocks = (tiles + R - 1) / R;
-  q.X = (size_t)lds_layout(true, (int)chunks, (int)mg, q.S, q.R).total <= kMaxLds;
-  q.lds = lds_layout(q.X, (int)chunks, (int)mg, q.S, q.R).total;
+  q.X = (size_t)lds_layout(true, (int)chunks, (int)mg, q.S, q.R, accs).total <= kMaxLds;
+  q.lds = lds_layout(q.X, (int)chunks, (int)mg, q.S, q.R, accs).total;
   q.fits = q.lds <= kMaxLds;
   return q;
 }
 
-template <int S, bool X, int OUT>
+template <int S, bool X, int OUT, bool RES = false>
 hipError_t launch_s(const GemmArgs& g, const Geometry& q, int64_t m0, int64_t mg,
                     int64_t row_bytes, hipStream_t stream) {
-  auto kfn = gemv_mfma_kernel<S, X, OUT>;
+  auto kfn = gemv_mfma_kernel<S, X, OUT, RES>;
   hipError_t e = hipFuncSetAttribute((const void*)kfn,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)q.lds);
   if (e != hipSuccess) return e;
@@ -450,37 +487,52 @@ hipError_t launch_s(const GemmArgs& g, const Geometry& q, int64_t m0, int64_t mg
   return hipGetLastError();
 }
 
-template <bool X, int OUT>
+template <bool X, int OUT, bool RES = false>
 hipError_t launch_x(const GemmArgs& g, const Geometry& q, int64_t m0, int64_t mg,
                     int64_t row_bytes, hipStream_t stream) {
   switch (q.S) {
-    case 1: return launch_s<1, X, OUT>(g, q, m0, mg, row_bytes, stream);
-    case 2: return launch_s<2, X, OUT>(g, q, m0, mg, row_bytes, stream);
-    case 4: return launch_s<4, X, OUT>(g, q, m0, mg, row_bytes, stream);
-    default: return launch_s<8, X, OUT>(g, q, m0, mg, row_bytes, stream);
+    case 1: return launch_s<1, X, OUT, RES>(g, q, m0, mg, row_bytes, stream);
+    case 2: return launch_s<2, X, OUT, RES>(g, q, m0, mg, row_bytes, stream);
+    case 4: return launch_s<4, X, OUT, RES>(g, q, m0, mg, row_bytes, stream);
+    default: return launch_s<8, X, OUT, RES>(g, q, m0, mg, row_bytes, stream);
   }
 }
 
-template <int OUT>
+template <int OUT, bool RES = false>
 hipError_t launch_out(const GemmArgs& g, hipStream_t stream) {
-  if (g.N >= (int64_t)1 << 29) return hipErrorInvalidValue;  // 32-bit byte offsets of w_alpha
+  if ((RES ? 2 : 1) * g.N >= (int64_t)1 << 29) return hipErrorInvalidValue;  // 32-bit offsets
   const int64_t row_bytes = (g.K + 63) / 64 * 8;
+  const int accs = RES ? 2 : 1;
   // Largest group of activation rows whose staging fits in LDS; one launch per
   // group.
   int64_t mg = g.M;
-  while (mg > 1 && !geometry(g.N, row_bytes, mg).fits) mg = (mg + 1) / 2;
+  while (mg > 1 && !geometry(g.N, row_bytes, mg, accs).fits) mg = (mg + 1) / 2;
   for (int64_t m0 = 0; m0 < g.M; m0 += mg) {
     const int64_t cnt = g.M - m0 < mg ? g.M - m0 : mg;
-    const Geometry q = geometry(g.N, row_bytes, cnt);
+    const Geometry q = geometry(g.N, row_bytes, cnt, accs);
     if (!q.fits) return hipErrorInvalidValue;
-    const hipError_t e = q.X ? launch_x<true, OUT>(g, q, m0, cnt, row_bytes, stream)
-                             : launch_x<false, OUT>(g, q, m0, cnt, row_bytes, stream);
+    const hipError_t e = q.X ? launch_x<true, OUT, RES>(g, q, m0, cnt, row_bytes, stream)
+                             : launch_x<false, OUT, RES>(g, q, m0, cnt, row_bytes, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 }  // namespace
+
+// Two-plane residual weights: g.N outputs (a multiple of 32), 2 g.N interleaved
+// plane rows; fp32 or bf16 output.
+hipError_t launch_gemv_mfma_residual(const GemmArgs& g, hipStream_t stream) {
+  if (g.N % 32 != 0) return hipErrorInvalidValue;
+  switch (g.y_dt) {
+    case Elt::F32:
+      return launch_out<(int)Elt::F32, true>(g, stream);
+    case Elt::BF16:
+      return launch_out<(int)Elt::BF16, true>(g, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_gemv_mfma(const GemmArgs& g, hipStream_t stream) {
   switch (g.y_dt) {

@@ -50,6 +50,8 @@ hipError_t launch_gemv_popcount(const GemmArgs& g, hipStream_t stream);
 // Two-plane residual weights, M <= 16 (g.N outputs, 2 g.N interleaved plane rows).
 hipError_t launch_gemv_popcount_residual(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemv_mfma(const GemmArgs& g, hipStream_t stream);
+// Two-plane residual weights, 2 <= M <= 16 (g.N outputs, 2 g.N interleaved plane rows).
+hipError_t launch_gemv_mfma_residual(const GemmArgs& g, hipStream_t stream);
 
 // Fused attention (attention.hip): ternary Q, K planes [heads * L, 16 bytes],
 // binary V^T planes [heads * D, L / 8 bytes], O [heads * L, D].

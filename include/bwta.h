@@ -168,11 +168,11 @@ bwta_status bwta_gemm_residual(const uint8_t* a_mask, const uint8_t* a_sign, con
                                int64_t ldy, void* stream);
 
 /* Decode with two-plane residual weights, 1 <= M <= 16: the product of
- * bwta_gemm_residual; for M <= 4 and row_bytes(K) a multiple of 16 by a kernel
- * that streams both planes from HBM once (each wave reads the four plane rows
- * of two adjacent outputs), otherwise by bwta_gemm_residual's kernel.
- * N a multiple of 32, M <= 16, and K > 64 unless that streaming kernel applies
- * (else BWTA_ERR_UNSUPPORTED); a_nnz is required. */
+ * bwta_gemm_residual by kernels that stream both planes from HBM once (M = 1
+ * with row_bytes(K) a multiple of 16: a popcount kernel that reads the four
+ * plane rows of two adjacent outputs per wave; otherwise the FP4 decode kernel
+ * with each wave on both plane tiles of its 16 outputs).  Any K > 0; N a
+ * multiple of 32 and M <= 16 (else BWTA_ERR_UNSUPPORTED); a_nnz is required. */
 bwta_status bwta_gemv_residual(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
                                const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha,
                                int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype,

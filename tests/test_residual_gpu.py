@@ -114,11 +114,12 @@ def test_gemm_residual_rejects_k64(bw):
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("M,N,K", [(1, 32, 128), (1, 64, 100), (3, 96, 100), (4, 128, 8192),
                                    (7, 64, 2000), (16, 160, 4100), (16, 32, 28672),
-                                   (2, 64, 129)])
+                                   (2, 64, 129), (1, 32, 64), (5, 64, 1), (16, 4096, 65536),
+                                   (13, 1024, 40000)])
 def test_gemv_residual(bw, oracle, M, N, K, out_dtype):
-    """Decode with two-plane weights: every output bit-exact.  M > 4, and K = 4100
-    and 129 (plane rows not a multiple of 16 bytes), take the two-plane GEMM
-    kernel; the rest the streaming kernel."""
+    """Decode with two-plane weights: every output bit-exact.  M = 1 with 16-byte
+    plane rows takes the popcount kernel, the rest the FP4 decode kernel (split K
+    for long rows, raw activation staging for M = 16 at K = 65536)."""
     x, w = inputs.random_linear(M * 5 + N + K, M, K, N)
     a = bw.bwta_ternarize_pack(to_dev(x))
     wp = bw.bwta_pack_weights_residual(to_dev(w))
@@ -131,11 +132,3 @@ def test_gemv_residual(bw, oracle, M, N, K, out_dtype):
     else:
         assert (y.view(np.uint32) == ref.view(np.uint32)).all()
 
-
-def test_gemv_residual_rejects_short_rows(bw):
-    """Plane rows of one 8-byte word (K <= 64) are not offered."""
-    x, w = inputs.random_linear(11, 1, 64, 32)
-    a = bw.bwta_ternarize_pack(to_dev(x))
-    wp = bw.bwta_pack_weights_residual(to_dev(w))
-    with pytest.raises(bw.BwtaError):
-        bw.bwta_gemv_residual(a, wp, "f32")
