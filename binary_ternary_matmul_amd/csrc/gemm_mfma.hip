@@ -207,21 +207,30 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
                  const uint8_t* __restrict__ b_mask, const uint8_t* __restrict__ b_sign,
                  const float* __restrict__ b_alpha, int64_t b_batch_rows, int64_t M, int64_t N,
                  int64_t row_bytes, int tiles_m, int tiles_n, void* __restrict__ Y, int64_t ldy,
-                 int64_t y_batch_stride) {
+                 int64_t y_batch_stride, int tile0) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = __lane_id();
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int r = lane & 31;
   const int g = lane >> 5;
 
-  // Blocks are dealt round-robin to the 8 XCDs; give each XCD a contiguous run
-  // of tiles (consecutive tile_n for the same tile_m) so that tiles sharing A
-  // rows share that XCD's L2.
-  const int nblk = tiles_m * tiles_n;
+  // The launch covers tiles tile0 .. tile0 + gridDim.x - 1 of the tile order
+  // below.  Blocks are dealt round-robin to the 8 XCDs; give each XCD a
+  // contiguous run of that order, whose tiles then share A and B panels in the
+  // XCD's L2.  Order: bands of kBand tile rows, column by column within a band,
+  // so a run of r tiles spans about kBand rows and r / kBand columns (LLaMA-7B
+  // gate/up, 172 tiles per XCD: 1 MB of A and 1.4 MB of B panels, against 0.25 MB
+  // and all 5.6 MB of B for row-major runs).
+  constexpr int kBand = 8;
+  const int nblk = (int)gridDim.x;
   int lin = blockIdx.x;
   if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-  const int tile_m = lin / tiles_n;
-  const int tile_n = lin - tile_m * tiles_n;
+  lin += tile0;
+  const int band = lin / (kBand * tiles_n);
+  const int band_rows = min(kBand, tiles_m - band * kBand);
+  const int in_band = lin - band * kBand * tiles_n;
+  const int tile_n = in_band / band_rows;
+  const int tile_m = band * kBand + (in_band - tile_n * band_rows);
   const int64_t b = blockIdx.z;
   const int64_t m0 = (int64_t)tile_m * WAVE_TILE;
   const int64_t n0 = (int64_t)tile_n * WAVE_TILE;
@@ -694,32 +703,61 @@ int choose_split(int64_t tiles, int64_t steps) {
 }
 
 template <bool B_TERNARY, int OUT, int S, bool RES = false>
-hipError_t launch_k(const GemmArgs& g, int64_t row_bytes, int64_t tm, int64_t tn,
-                    hipStream_t stream) {
+hipError_t launch_k(const GemmArgs& g, int64_t row_bytes, int64_t tm, int64_t tn, int64_t tile0,
+                    int64_t tiles, hipStream_t stream) {
   size_t lds = (size_t)S * kRing * Stage<B_TERNARY>::kBytes;
   if (S > 1 && lds < kXchgBytes) lds = kXchgBytes;
   auto kfn = gemm_mfma_kernel<B_TERNARY, OUT, S, RES>;
   hipError_t e =
       hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kfn, dim3((unsigned)(tm * tn), 1, (unsigned)g.batch), dim3(S * kWave), lds,
+  hipLaunchKernelGGL(kfn, dim3((unsigned)tiles, 1, (unsigned)g.batch), dim3(S * kWave), lds,
                      stream, g.a_mask, g.a_sign, g.a_alpha, g.a_batch_rows, g.b_mask, g.b_sign,
                      g.b_alpha, g.b_batch_rows, g.M, g.N, row_bytes, (int)tm, (int)tn, g.Y, g.ldy,
-                     g.y_batch_stride);
+                     g.y_batch_stride, (int)tile0);
   return hipGetLastError();
 }
 
 template <bool B_TERNARY, int OUT, bool RES = false>
 hipError_t launch_s(const GemmArgs& g, int S, int64_t row_bytes, int64_t tm, int64_t tn,
-                    hipStream_t stream) {
+                    int64_t tile0, int64_t tiles, hipStream_t stream) {
   switch (S) {
     case 1:
-      return launch_k<B_TERNARY, OUT, 1, RES>(g, row_bytes, tm, tn, stream);
+      return launch_k<B_TERNARY, OUT, 1, RES>(g, row_bytes, tm, tn, tile0, tiles, stream);
     case 2:
-      return launch_k<B_TERNARY, OUT, 2, RES>(g, row_bytes, tm, tn, stream);
+      return launch_k<B_TERNARY, OUT, 2, RES>(g, row_bytes, tm, tn, tile0, tiles, stream);
     default:
-      return launch_k<B_TERNARY, OUT, 4, RES>(g, row_bytes, tm, tn, stream);
+      return launch_k<B_TERNARY, OUT, 4, RES>(g, row_bytes, tm, tn, tile0, tiles, stream);
   }
+}
+
+// Launches of one product, against the 1024 SIMDs (one wave each):
+// * fewer than 1024 tiles: one launch, K split over S waves where that fills
+//   more SIMDs (q, o, down of LLaMA-7B: 512 tiles, 30.5 us with S = 2 against
+//   36.6 unsplit);
+// * otherwise whole rounds of 1024 unsplit tiles, and a last partial round of
+//   at most 512 tiles as a second launch with K split in two, which takes about
+//   half as long as a round (LLaMA-7B gate/up: 1024 + 352 tiles);
+// * batches and remainders above 512 unsplit: splitting every tile only adds
+//   exchange work there (gate/up 80 us unsplit, 84 / 118 us with S = 2 / 4 on
+//   every tile).
+template <bool B_TERNARY, int OUT, bool RES = false>
+hipError_t launch_plan(const GemmArgs& g, int64_t row_bytes, int64_t tm, int64_t tn,
+                       hipStream_t stream) {
+  const int64_t simds = 1024;
+  const int64_t steps = (row_bytes / 8 + 3) / 4;
+  const int64_t tiles = tm * tn;
+  if (tiles * g.batch < simds)
+    return launch_s<B_TERNARY, OUT, RES>(g, choose_split(tiles * g.batch, steps), row_bytes, tm,
+                                         tn, 0, tiles, stream);
+  const int64_t rem = tiles % simds;
+  if (g.batch == 1 && rem > 0 && rem <= simds / 2 && steps >= 4) {
+    const hipError_t e =
+        launch_s<B_TERNARY, OUT, RES>(g, 1, row_bytes, tm, tn, 0, tiles - rem, stream);
+    if (e != hipSuccess) return e;
+    return launch_s<B_TERNARY, OUT, RES>(g, 2, row_bytes, tm, tn, tiles - rem, rem, stream);
+  }
+  return launch_s<B_TERNARY, OUT, RES>(g, 1, row_bytes, tm, tn, 0, tiles, stream);
 }
 
 template <bool B_TERNARY>
@@ -727,20 +765,13 @@ hipError_t launch_b(const GemmArgs& g, hipStream_t stream) {
   const int64_t row_bytes = (g.K + 63) / 64 * 8;
   const int64_t tm = (g.M + WAVE_TILE - 1) / WAVE_TILE;
   const int64_t tn = (g.N + WAVE_TILE - 1) / WAVE_TILE;
-  const int64_t steps = (row_bytes / 8 + 3) / 4;
-  // From 1024 tiles on (a full round of single-wave tiles) splitting K only
-  // adds exchange work: LLaMA-7B gate/up (1376 tiles) 80 us unsplit, 84 / 118 us
-  // with S = 2 / 4; below that the split fills the idle SIMDs (q, o, down:
-  // 512 tiles, 30.5 us with S = 2 against 36.6 unsplit).
-  const int64_t tiles = tm * tn * g.batch;
-  const int S = tiles >= 1024 ? 1 : choose_split(tiles, steps);
   switch (g.y_dt) {
     case Elt::F32:
-      return launch_s<B_TERNARY, (int)Elt::F32>(g, S, row_bytes, tm, tn, stream);
+      return launch_plan<B_TERNARY, (int)Elt::F32>(g, row_bytes, tm, tn, stream);
     case Elt::BF16:
-      return launch_s<B_TERNARY, (int)Elt::BF16>(g, S, row_bytes, tm, tn, stream);
+      return launch_plan<B_TERNARY, (int)Elt::BF16>(g, row_bytes, tm, tn, stream);
     default:
-      return launch_s<B_TERNARY, (int)Elt::I32>(g, S, row_bytes, tm, tn, stream);
+      return launch_plan<B_TERNARY, (int)Elt::I32>(g, row_bytes, tm, tn, stream);
   }
 }
 
@@ -758,14 +789,9 @@ hipError_t launch_gemm_mfma_residual(const GemmArgs& g, hipStream_t stream) {
   const int64_t row_bytes = (g.K + 63) / 64 * 8;
   const int64_t tm = (g.M + WAVE_TILE - 1) / WAVE_TILE;
   const int64_t tn = (g.N + WAVE_TILE - 1) / WAVE_TILE;
-  const int64_t steps = (row_bytes / 8 + 3) / 4;
-  // As for one plane (two-plane LLaMA-7B gate: 125 us unsplit, 163 / 225 us
-  // with S = 2 / 4).
-  const int64_t tiles = tm * tn * g.batch;
-  const int S = tiles >= 1024 ? 1 : choose_split(tiles, steps);
-  return g.y_dt == Elt::F32
-             ? launch_s<false, (int)Elt::F32, true>(g, S, row_bytes, tm, tn, stream)
-             : launch_s<false, (int)Elt::BF16, true>(g, S, row_bytes, tm, tn, stream);
+  // Launches as for one plane.
+  return g.y_dt == Elt::F32 ? launch_plan<false, (int)Elt::F32, true>(g, row_bytes, tm, tn, stream)
+                            : launch_plan<false, (int)Elt::BF16, true>(g, row_bytes, tm, tn, stream);
 }
 
 }  // namespace bwta

@@ -162,6 +162,48 @@ def test_gemm_ldy(bw, oracle):
         assert (o[:, :N] == ref["y"]).all() and (o[:, N:] == -7.0).all()
 
 
+# Grids of more 128 x 128 output tiles than the chip's 1024 SIMDs: whole rounds
+# run one tile per wave over all of K, the last partial round (at most 512
+# tiles) splits each tile's K range over two waves, both kinds of blocks in one
+# launch.  Outputs start as a sentinel, every output is checked against the
+# properties |acc| <= nnz and acc = nnz (mod 2), and all rows against the oracle
+# on two columns of every 128-column tile.
+GRID_SHAPES = [(2048, 8300, 1000),   # 16 x 65 tiles = 1024 + 16; ragged N, ragged K
+               (1900, 8960, 1536)]   # 15 x 70 tiles = 1024 + 26; ragged M
+
+
+def _grid_columns(N, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cols = [min(N - 1, 128 * j + int(c)) for j in range((N + 127) // 128)
+            for c in rng.choice(128, size=2, replace=False)]
+    return np.unique(np.array(cols + [N - 1], dtype=np.int64))
+
+
+@pytest.mark.parametrize("M,N,K", GRID_SHAPES)
+def test_gemm_grid_rounds(bw, oracle, M, N, K):
+    import torch
+    x = _x(M + N + K, M, K, True)
+    w = _w(N + 3 * K, N, K)
+    a = bw.bwta_ternarize_pack(to_dev(x))
+    wp = bw.bwta_pack_weights(to_dev(w))
+    t, aa, nnz = oracle.ternarize(x)
+    s, ab = oracle.binarize(w)
+    C = _grid_columns(N, M + K)
+    ref_acc = oracle.matmul_i32(t, s[C], threads=8)
+    acc = torch.full((M, N), 0x7FFFFFFF, dtype=torch.int32, device="cuda")
+    acc = to_host(bw.bwta_gemm(a, wp, out_dtype="i32", algo="mfma", out=acc)).astype(np.int64)
+    nz = nnz.astype(np.int64)[:, None]
+    assert (np.abs(acc) <= nz).all() and ((acc - nz) % 2 == 0).all(), "an output breaks |acc| <= nnz"
+    assert (acc[:, C] == ref_acc).all(), f"{(acc[:, C] != ref_acc).sum()} accumulators differ"
+    y = torch.full((M, N), float("nan"), device="cuda")
+    y = to_host(bw.bwta_gemm(a, wp, out_dtype="f32", algo="mfma", out=y))
+    assert not np.isnan(y).any(), "outputs left unwritten"
+    ref = oracle.scale(ref_acc, aa, ab[C])
+    assert (y[:, C].view(np.uint32) == ref.view(np.uint32)).all()
+    yb = to_host(bw.bwta_gemm(a, wp, out_dtype="bf16", algo="mfma"))
+    assert (yb[:, C] == oracle.to_bf16(ref)).all()
+
+
 @pytest.mark.parametrize("algo", ["popcount", "mfma", "mfma_i8", "auto"])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16])
 @pytest.mark.parametrize("N,K", [(1000, 1024), (513, 8192), (300, 28672), (77, 200)])

@@ -102,6 +102,28 @@ def test_gemm_residual_ldy(bw, oracle):
     assert (got[:, N:] == 7.0).all()
 
 
+def test_gemm_residual_grid_rounds(bw, oracle):
+    """16 x 65 plane tiles (4160 outputs, 8320 plane rows): 1024 tiles one per wave,
+    the last 16 split over K; NaN-filled output, all rows on two columns of every
+    64-output tile."""
+    import torch
+    M, N, K = 2048, 4160, 1000
+    x, w = inputs.random_linear(4242, M, K, N)
+    a = bw.bwta_ternarize_pack(to_dev(x))
+    wp = bw.bwta_pack_weights_residual(to_dev(w))
+    out = torch.full((M, N), float("nan"), device="cuda")
+    y = to_host(bw.bwta_gemm_residual(a, wp, "f32", out=out))
+    assert not np.isnan(y).any(), "outputs left unwritten"
+    rng = np.random.default_rng(17)
+    C = np.unique(np.concatenate([64 * j + rng.choice(64, size=2, replace=False)
+                                  for j in range(N // 64)] + [[N - 1]]))
+    t, aa, _ = oracle.ternarize(x)
+    s1, a1, s2, a2 = oracle.binarize_residual(w)
+    ref = oracle.scale_residual(oracle.matmul_i32(t, s1[C], threads=8),
+                                oracle.matmul_i32(t, s2[C], threads=8), aa, a1[C], a2[C])
+    assert (y[:, C].view(np.uint32) == ref.view(np.uint32)).all()
+
+
 def test_gemm_residual_rejects_k64(bw):
     """The FP4 kernel needs plane rows of 16 bytes or more (K > 64)."""
     x, w = inputs.random_linear(9, 4, 64, 32)
