@@ -3,18 +3,21 @@
 One step = one LLaMA-7B-shaped decoder layer's linears at prefill (M = 2048
 tokens): ternarize+pack the four bf16 activation inputs (attention input,
 attention output, MLP input, MLP activation) and run the seven binary x ternary
-GEMMs (q, k, v, o: 4096 -> 4096; gate, up: 4096 -> 11008; down: 11008 -> 4096)
-with the fused bf16 epilogue.  Weights are packed once before timing (as for a
-deployed model).  `value` is the step's int8-equivalent throughput in TOPS
-(2*M*N*K over the seven GEMMs per step time, ternarize included).
+linears (q, k, v, o: 4096 -> 4096; gate, up: 4096 -> 11008; down: 11008 -> 4096)
+with the fused bf16 epilogue, as four products: the projections that read the same
+input have their packed weights stacked along N (qkv 4096 -> 12288, gate_up
+4096 -> 22016), which gives the same outputs as separate products.  Weights are
+packed once before timing (as for a deployed model).  `value` is the step's
+int8-equivalent throughput in TOPS (2*M*N*K over the seven linears per step time,
+ternarize included).
 
 The same run also measures, each in its own object on the JSON line:
   gemv       decode GEMV/skinny GEMM, LLaMA2-70B shapes, M in {1, 4, 16}: HBM GB/s
              with >= 20 rotating weight copies so every launch reads from HBM
   attention  32 heads x 2048 x 128: ternarize Q, K -> Q K^T (int32 scores) and
              ternarize P -> pack V^T -> P V
-  mfma_i8    the int8 MFMA GEMM on the same seven GEMMs (the FP4 kernel's alternative)
-  popcount   the VALU popcount GEMM on the same seven GEMMs (the alternative to MFMA)
+  mfma_i8    the int8 MFMA GEMM on the same products (the FP4 kernel's alternative)
+  popcount   the VALU popcount GEMM on the same products (the alternative to MFMA)
   bert       BERT-base encoder linears, M = 4096, fp32 in, bf16 out
   roofline   the FP4 MFMA GEMM kernel's achieved TOPS against the dense FP4 peak
              (gemm_frac_of_int8_peak gives the same against the int8 peak)
@@ -123,7 +126,7 @@ def profiled_traffic(key):
 def bench_prefill(bw, steps, warmup, M=2048):
     import torch
     from binary_ternary_matmul_amd import inputs
-    acts, lins = inputs.llama7b_prefill(M)
+    acts, lins = inputs.llama7b_products(M)
     log(f"[prefill] generating inputs M={M}")
     X = {name: dev(gen()) for name, gen in acts.items()}
     W = {}
@@ -176,7 +179,7 @@ def bench_prefill(bw, steps, warmup, M=2048):
 
 
 def bench_algo(bw, pre, algo, reps=5):
-    """The same seven GEMMs with another kernel family (popcount, int8 MFMA)."""
+    """The same four products with another kernel family (popcount, int8 MFMA)."""
     import torch
     from binary_ternary_matmul_amd import inputs
     planes = {name: bw.bwta_ternarize_pack(x) for name, x in pre["X"].items()}
@@ -197,11 +200,11 @@ def bench_algo(bw, pre, algo, reps=5):
 
 
 def bench_residual(bw, pre, reps=5):
-    """The same seven GEMMs with two-plane residual weights (bwta_gemm_residual):
+    """The same four products with two-plane residual weights (bwta_gemm_residual):
     both planes in one pass; ops counted per plane (twice the single-plane ops)."""
     import torch
     from binary_ternary_matmul_amd import inputs
-    acts, lins = inputs.llama7b_prefill(pre["M"])
+    acts, lins = inputs.llama7b_products(pre["M"])
     planes = {name: bw.bwta_ternarize_pack(x) for name, x in pre["X"].items()}
     res, tot_ops, tot_ms = {}, 0.0, 0.0
     for lin in lins:
@@ -508,6 +511,7 @@ def main():
         print(json.dumps({"attention": bench_attention(bw)}), flush=True)
         return
 
+    from binary_ternary_matmul_amd import inputs
     pre = bench_prefill(bw, args.steps, args.warmup)
     achieved = pre["ops"] / (pre["gemm_ms"] * 1e-3) / 1e12
     line = {
@@ -525,6 +529,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama7b_prefill_layer_linears", "tokens": pre["M"],
                    "gemms": {k: [v["M"], v["N"], v["K"]] for k, v in pre["per_gemm"].items()},
+                   "stacked": {name: list(parts) for name, parts in inputs.LLAMA7B_PRODUCTS
+                               if len(parts) > 1},
                    "activations": "bf16 Student-t(3), 1% outlier channels x50",
                    "weights": "N(0,0.02) packed to 1 bit", "out": "bf16",
                    "ops_per_step": pre["ops"]},

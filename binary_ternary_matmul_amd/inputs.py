@@ -116,7 +116,8 @@ LLAMA7B_SHAPES = [("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o",
 # which activation feeds each projection: q/k/v share the attention input, gate/up
 # share the MLP input; o and down have their own.
 LLAMA7B_INPUTS = {"q": "attn_in", "k": "attn_in", "v": "attn_in", "o": "attn_out",
-                  "gate": "mlp_in", "up": "mlp_in", "down": "mlp_act"}
+                  "gate": "mlp_in", "up": "mlp_in", "down": "mlp_act",
+                  "qkv": "attn_in", "gate_up": "mlp_in"}
 
 
 def llama7b_prefill(M: int = 2048, out_dtype: str = "bf16") -> tuple[dict, list[Linear]]:
@@ -135,6 +136,29 @@ def llama7b_prefill(M: int = 2048, out_dtype: str = "bf16") -> tuple[dict, list[
         lins.append(Linear(name, M, K, N, "bf16", out_dtype, acts[LLAMA7B_INPUTS[name]],
                            _mk_w(ss[4 + j], N, K, 0.02)))
     return acts, lins
+
+
+# The seven linears as the four products a layer runs: projections that read the
+# same activation have their weights stacked along N (q/k/v into [12288, 4096],
+# gate/up into [22016, 4096]).  Every weight row keeps its own plane row and
+# scale, so a stacked product equals its linears side by side.
+LLAMA7B_PRODUCTS = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")),
+                    ("down", ("down",))]
+
+
+def stacked(name: str, lins: list[Linear]) -> Linear:
+    """One Linear whose weights are those of `lins` (same activation) stacked along N."""
+    first = lins[0]
+    gens = [lin._gen_w for lin in lins]
+    return Linear(name, first.M, first.K, sum(lin.N for lin in lins), first.x_dtype,
+                  first.out_dtype, first._gen_x, lambda: np.concatenate([g() for g in gens]))
+
+
+def llama7b_products(M: int = 2048, out_dtype: str = "bf16") -> tuple[dict, list[Linear]]:
+    """The LLaMA-7B prefill linears as the four stacked products (LLAMA7B_PRODUCTS)."""
+    acts, lins = llama7b_prefill(M, out_dtype)
+    by = {lin.name: lin for lin in lins}
+    return acts, [stacked(name, [by[p] for p in parts]) for name, parts in LLAMA7B_PRODUCTS]
 
 
 LLAMA70B_DECODE_SHAPES = [("gate_up", 8192, 28672), ("down", 28672, 8192)]

@@ -121,6 +121,17 @@ def test_full_llama7b_prefill(bw, oracle, i):
     _sampled_linear(bw, oracle, lin, x, "mfma", "bf16", seed=200 + i)
 
 
+@pytest.mark.parametrize("name", ["qkv", "gate_up"])
+def test_full_llama7b_stacked(bw, oracle, name):
+    """The stacked products bench.py times (q/k/v weights as one [12288, 4096],
+    gate/up as one [22016, 4096]), bf16 out, algo mfma: planes in full, a sample of
+    outputs (qkv runs as two launches, gate_up as one of three rounds)."""
+    acts, prods = inputs.llama7b_products()
+    lin = [p for p in prods if p.name == name][0]
+    x = acts[inputs.LLAMA7B_INPUTS[name]]()
+    _sampled_linear(bw, oracle, lin, x, "mfma", "bf16", seed=260 + len(name))
+
+
 @pytest.mark.parametrize("shape", [n for n, _, _ in inputs.LLAMA70B_DECODE_SHAPES])
 def test_full_llama70b_decode(bw, oracle, shape):
     """Decode GEMV at M = 1, 4, 16 on the full 70B-shaped weights, algo auto,
