@@ -225,10 +225,6 @@ bwta_status bwta_gemm_residual(const uint8_t* a_mask, const uint8_t* a_sign, con
   if (ldy < N) return fail(BWTA_ERR_INVALID, "ldy (%lld) < N (%lld)", (long long)ldy, (long long)N);
   if (N % 32 != 0)
     return fail(BWTA_ERR_UNSUPPORTED, "N = %lld is not a multiple of 32", (long long)N);
-  // The FP4 kernel's 16-byte DMA window needs rows of 16 bytes or more (K > 64);
-  // bwta_gemm routes shorter rows to the popcount kernel, which has no
-  // two-plane mode.
-  if (K <= 64) return fail(BWTA_ERR_UNSUPPORTED, "K = %lld (two-plane product needs K > 64)", (long long)K);
   if (M == 0 || N == 0) return BWTA_OK;  // empty: pointers may be NULL
   BWTA_TRY(check_plane(a_mask, "a_mask"));
   BWTA_TRY(check_plane(a_sign, "a_sign"));
@@ -239,7 +235,11 @@ bwta_status bwta_gemm_residual(const uint8_t* a_mask, const uint8_t* a_sign, con
   if (!aligned(Y, dtype_size(y_dtype))) return fail(BWTA_ERR_ALIGN, "Y is not aligned to its element");
   bwta::GemmArgs g{a_mask, a_sign, a_alpha, a_nnz, 0, nullptr, w_sign, w_alpha, 0,
                    1, M, 2 * N, K, Y, elt(y_dtype), ldy, 0};
-  return from_hip(bwta::launch_gemm_mfma_residual(g, static_cast<hipStream_t>(stream)),
+  // The FP4 kernel's 16-byte DMA window needs plane rows of 16 bytes or more
+  // (K > 64); rows of one word take the popcount kernel.
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return from_hip(K <= 64 ? bwta::launch_gemm_residual_word(g, st)
+                          : bwta::launch_gemm_mfma_residual(g, st),
                   "bwta_gemm_residual launch");
 }
 

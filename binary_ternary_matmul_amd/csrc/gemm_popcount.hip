@@ -355,7 +355,65 @@ hipError_t launch_gemv_out(const GemmArgs& g, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+// Two-plane products whose plane rows are one 64-bit word (K <= 64), the rows
+// the FP4 kernel's 16-byte window does not take.  One thread per output column n
+// holds the words of its two plane rows (64 (n / 32) + n % 32 and 32 further,
+// consecutive for consecutive n) and walks a range of activation rows:
+//   acc_i = popc(m) - 2 popc(m & (s ^ w_i)),
+//   y = fl32(fl32(acc1 * fl32(aa * a1)) + fl32(acc2 * fl32(aa * a2))).
+template <int OUT>
+__global__ void __launch_bounds__(256)
+residual_word_kernel(const uint64_t* __restrict__ a_mask, const uint64_t* __restrict__ a_sign,
+                     const float* __restrict__ a_alpha, int64_t M,
+                     const uint64_t* __restrict__ w_sign, const float* __restrict__ w_alpha,
+                     int64_t N, void* __restrict__ Y, int64_t ldy, int64_t rows_per_block) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const int64_t pn = 64 * (n >> 5) + (n & 31);
+  const uint64_t w1 = w_sign[pn], w2 = w_sign[pn + 32];
+  const float a1 = w_alpha[pn], a2 = w_alpha[pn + 32];
+  const int64_t m0 = (int64_t)blockIdx.y * rows_per_block;
+  const int64_t m1 = m0 + rows_per_block < M ? m0 + rows_per_block : M;
+  for (int64_t m = m0; m < m1; ++m) {
+    const uint64_t mk = a_mask[m], sg = a_sign[m];
+    // (HIP's __popcll returns an unsigned int: count in int so nz - 2 c can go negative)
+    const int nz = (int)__popcll(mk);
+    const float acc1 = (float)(nz - 2 * (int)__popcll(mk & (sg ^ w1)));
+    const float acc2 = (float)(nz - 2 * (int)__popcll(mk & (sg ^ w2)));
+    const float aa = a_alpha[m];
+    const float y = acc1 * (aa * a1) + acc2 * (aa * a2);
+    if constexpr (OUT == (int)Elt::F32)
+      static_cast<float*>(Y)[m * ldy + n] = y;
+    else
+      static_cast<__bf16*>(Y)[m * ldy + n] = (__bf16)y;
+  }
+}
+
+template <int OUT>
+hipError_t launch_residual_word_out(const GemmArgs& g, hipStream_t stream) {
+  const int64_t N = g.N / 2;  // outputs
+  int64_t rows = g.M < 16 ? g.M : 16;  // activation rows per block
+  if ((g.M + rows - 1) / rows > 65535) rows = (g.M + 65534) / 65535;
+  const int64_t gy = (g.M + rows - 1) / rows;
+  hipLaunchKernelGGL(residual_word_kernel<OUT>, dim3((unsigned)((N + 255) / 256), (unsigned)gy),
+                     dim3(256), 0, stream, reinterpret_cast<const uint64_t*>(g.a_mask),
+                     reinterpret_cast<const uint64_t*>(g.a_sign), g.a_alpha, g.M,
+                     reinterpret_cast<const uint64_t*>(g.b_sign), g.b_alpha, N, g.Y, g.ldy, rows);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// Two-plane product for K <= 64: g.N counts plane rows (twice the outputs, a
+// multiple of 64), one 8-byte word per plane row.
+hipError_t launch_gemm_residual_word(const GemmArgs& g, hipStream_t stream) {
+  if (g.K > 64 || g.N % 64 != 0) return hipErrorInvalidValue;
+  switch (g.y_dt) {
+    case Elt::F32: return launch_residual_word_out<(int)Elt::F32>(g, stream);
+    case Elt::BF16: return launch_residual_word_out<(int)Elt::BF16>(g, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_gemm_popcount(const GemmArgs& g, hipStream_t stream) {
   switch (g.y_dt) {

@@ -46,6 +46,8 @@ hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemm_mfma_residual(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemm_mfma_i8(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemm_popcount(const GemmArgs& g, hipStream_t stream);
+// Two-plane residual weights with K <= 64 (one word per plane row; g.N = 2 x outputs).
+hipError_t launch_gemm_residual_word(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemv_popcount(const GemmArgs& g, hipStream_t stream);
 // Two-plane residual weights, M <= 16 (g.N outputs, 2 g.N interleaved plane rows).
 hipError_t launch_gemv_popcount_residual(const GemmArgs& g, hipStream_t stream);

@@ -159,9 +159,10 @@ bwta_status bwta_gemm(const uint8_t* a_mask, const uint8_t* a_sign, const float*
  *   Y[m][n] = fl32(fl32(acc1 * fl32(alpha_a[m] * alpha1[n]))
  *               + fl32(acc2 * fl32(alpha_a[m] * alpha2[n])))
  * with acc_i = sum_k t[m][k] * s_i[n][k], both planes multiplied in one pass on
- * the FP4 matrix cores.  Y: M x N, leading dimension ldy >= N, BWTA_F32 or
- * BWTA_BF16.  N must be a multiple of 32 and K > 64 (else
- * BWTA_ERR_UNSUPPORTED); a_nnz is not used and may be NULL. */
+ * the FP4 matrix cores (K <= 64, plane rows of one word: a popcount kernel).
+ * Y: M x N, leading dimension ldy >= N, BWTA_F32 or BWTA_BF16.  N must be a
+ * multiple of 32 (else BWTA_ERR_UNSUPPORTED); a_nnz is not used and may be
+ * NULL. */
 bwta_status bwta_gemm_residual(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
                                const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha,
                                int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype,

@@ -173,7 +173,6 @@ def test_residual_validation(L):
     def call(M=4, N=64, K=128, Y=A, dt=0, ldy=64, w_sign=A, a_nnz=0):
         return g(P(A), P(A), P(A), P(a_nnz), P(w_sign), P(A), M, N, K, P(Y), dt, ldy, P(0))
     assert call(N=48) == UNSUPPORTED
-    assert call(K=64) == UNSUPPORTED
     assert call(M=-1) == INVALID
     assert call(K=0) == INVALID
     assert call(dt=2) == INVALID                                      # scaled outputs only
