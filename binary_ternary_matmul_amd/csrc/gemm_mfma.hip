@@ -195,6 +195,52 @@ __device__ __forceinline__ v16f mfma_fp4(v4i a, v4i b, v16f c) {
 // rows, 64 KiB in all (within the rings whenever S > 1).
 constexpr size_t kXchgBytes = (size_t)TILES * TILES * 16 * kWave * 4;
 
+// Store row block i (32 rows x 32 NJ columns) of a complete tile from the
+// lanes' output words o[j][qh][0..3] (row r, columns 32 j + 8 qh + 4 g + 0..3;
+// ES-byte elements, bf16 pairs packed per 32-bit word on the way).  In that layout
+// a store instruction covers 32 rows x 4 elements, one L2 request per row, so the
+// block goes through LDS (stg: the wave's own, free staging area) row-major, and
+// each 16-byte store instruction then writes whole rows: 64 lanes x 16 bytes
+// over 64 lanes / (2 NJ ES) rows, a quarter to an eighth of the requests.
+template <int NJ, int ES>
+__device__ __forceinline__ void store_row_block(const uint32_t (&o)[TILES][4][4], uint8_t* stg,
+                                                int r, int g, int lane,
+                                                __amdgpu_buffer_rsrc_t yrs, uint32_t ldb, int i) {
+  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  constexpr int RB = 32 * NJ * ES;  // bytes of one row of the block
+  constexpr int PITCH = RB + 16;    // staged row pitch (rows on different banks)
+  constexpr int LPR = RB / 16;      // lanes per row in a 16-byte read
+  constexpr int RPI = kWave / LPR;  // rows per store instruction
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int qh = 0; qh < 4; ++qh) {
+      const uint32_t(&w)[4] = o[j][qh];
+      uint8_t* dst = stg + r * PITCH + (32 * j + 8 * qh + 4 * g) * ES;
+      if constexpr (ES == 4)
+        *reinterpret_cast<v4u*>(dst) = v4u{w[0], w[1], w[2], w[3]};
+      else
+        *reinterpret_cast<v2u*>(dst) = v2u{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+    }
+  // other lanes read what this lane wrote: complete the writes first
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  const int soff = (int)__builtin_amdgcn_readfirstlane(32 * i * ldb);
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int rr = it * RPI + lane / LPR;
+    const int cb = (lane % LPR) * 16;
+    const v4u d = *reinterpret_cast<const v4u*>(stg + rr * PITCH + cb);
+    __builtin_amdgcn_raw_buffer_store_b128(d, yrs, (int)(rr * ldb + cb), soff, 0);
+  }
+  // and the reads before the next row block overwrites the stage
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // RES: B holds two binary planes per weight row, interleaved in groups of 32
 // rows (plane 1 of weight rows 32p..32p+31, then plane 2 of the same rows), so
 // MFMA column tiles 2jj and 2jj + 1 of a wave tile carry the two accumulators of
@@ -527,12 +573,9 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   // Epilogue straight from the registers of the owned tile rows: y = acc *
   // (alpha_a[row] * alpha_b[col]) in fp32 (the product of the scales first),
   // bf16 rounded to nearest even (v_cvt_pk_bf16_f32), or the int32 sum itself.
-  // Each store writes a lane's 4 consecutive columns (8 or 16 bytes).  Complete
-  // tiles store through a buffer descriptor of the tile origin: the lane's
-  // offset in a VGPR, the tile row in an SGPR, the column block as an
-  // immediate.  Edge tiles check every element.
-  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  // Complete tiles store row blocks through LDS (store_row_block: whole rows per
+  // 16-byte store, through a buffer descriptor of the tile origin); edge tiles
+  // store a lane's elements one by one with every element checked.
   constexpr int ES = OUT == (int)Elt::BF16 ? 2 : 4;
   char* ytile = static_cast<char*>(Y) + (b * y_batch_stride + m0 * ldy + (RES ? n0 / 2 : n0)) * ES;
   // The column scales of this lane's 64 columns, read once.
@@ -553,7 +596,6 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
                     (int64_t)WAVE_TILE * ldy * ES < (int64_t)0x7FFFFFFF;
   const __amdgpu_buffer_rsrc_t yrs = uniform_rsrc(ytile);
   const uint32_t ldb = (uint32_t)(ldy * ES);
-  const uint32_t lane_off = r * ldb + 4 * g * ES;
   if constexpr (RES) {
     static_assert(OUT != (int)Elt::I32, "two-plane products are scaled");
 
@@ -574,7 +616,7 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
       const int i = (ii + rot) & 3;
       const int row = 32 * i + r;
       const float aa = row < m_valid ? a_alpha[b * a_batch_rows + m0 + row] : 0.0f;
-      uint32_t o[TILES / 2][4][4];
+      uint32_t o[TILES][4][4];  // the first TILES / 2 column blocks are used
 #pragma unroll
       for (int jj = 0; jj < TILES / 2; ++jj)
 #pragma unroll
@@ -590,21 +632,7 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
               o[jj][qh][u] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y);
           }
       if (full) {
-        const int soff = (int)__builtin_amdgcn_readfirstlane(32 * i * ldb);
-#pragma unroll
-        for (int jj = 0; jj < TILES / 2; ++jj)
-#pragma unroll
-          for (int qh = 0; qh < 4; ++qh) {
-            const int voff = (int)(lane_off + (32 * jj + 8 * qh) * ES);
-            const uint32_t(&w)[4] = o[jj][qh];
-            if constexpr (ES == 4) {
-              const v4u d = {w[0], w[1], w[2], w[3]};
-              __builtin_amdgcn_raw_buffer_store_b128(d, yrs, voff, soff, 0);
-            } else {
-              const v2u d = {w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
-              __builtin_amdgcn_raw_buffer_store_b64(d, yrs, voff, soff, 0);
-            }
-          }
+        store_row_block<TILES / 2, ES>(o, ring, r, g, lane, yrs, ldb, i);
       } else if (row < m_valid) {
 #pragma unroll
         for (int jj = 0; jj < TILES / 2; ++jj)
@@ -649,21 +677,7 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
             o[j][qh][u] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(a * (aa * ab[j][qh][u])));
         }
     if (full) {
-      const int soff = (int)__builtin_amdgcn_readfirstlane(32 * i * ldb);
-#pragma unroll
-      for (int j = 0; j < TILES; ++j)
-#pragma unroll
-        for (int qh = 0; qh < 4; ++qh) {
-          const int voff = (int)(lane_off + (32 * j + 8 * qh) * ES);
-          const uint32_t(&w)[4] = o[j][qh];
-          if constexpr (ES == 4) {
-            const v4u d = {w[0], w[1], w[2], w[3]};
-            __builtin_amdgcn_raw_buffer_store_b128(d, yrs, voff, soff, 0);
-          } else {
-            const v2u d = {w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
-            __builtin_amdgcn_raw_buffer_store_b64(d, yrs, voff, soff, 0);
-          }
-        }
+      store_row_block<TILES, ES>(o, ring, r, g, lane, yrs, ldb, i);
     } else if (row < m_valid) {
 #pragma unroll
       for (int j = 0; j < TILES; ++j)
