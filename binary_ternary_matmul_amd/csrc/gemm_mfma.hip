@@ -64,12 +64,16 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 // LDS staging of one step (256 k = 32 bytes of each of 128 rows per plane).
 // Plane order in a stage: A mask, A sign, B sign, [B mask].
-template <bool B_TERNARY>
+// PAIR: two waves of a block on tiles (m, 2c) and (m, 2c + 1) share A; a slot
+// holds A mask, A sign, B sign of wave 0 and of wave 1, [B mask of each], and
+// each wave loads one A plane and its own B planes.
+template <bool B_TERNARY, bool PAIR = false>
 struct Stage {
   static constexpr int kPlane = WAVE_TILE * 32;
-  static constexpr int kPlanes = B_TERNARY ? 4 : 3;
+  static constexpr int kBPlanes = B_TERNARY ? 2 : 1;
+  static constexpr int kPlanes = PAIR ? 2 + 2 * kBPlanes : 2 + kBPlanes;
   static constexpr int kBytes = kPlane * kPlanes;
-  static constexpr int kLoads = 4 * kPlanes;  // DMA instructions per step and lane
+  static constexpr int kLoads = 4 * (PAIR ? 1 + kBPlanes : kPlanes);  // DMA instructions per step and lane
 };
 
 // Copy 32 bytes (one 256-k step) of each of 128 rows of one plane into LDS
@@ -246,8 +250,8 @@ __device__ __forceinline__ void store_row_block(const uint32_t (&o)[TILES][4][4]
 // MFMA column tiles 2jj and 2jj + 1 of a wave tile carry the two accumulators of
 // the same 32 outputs in the same lanes, and the epilogue writes
 // y = acc1 * (alpha_a * alpha1) + acc2 * (alpha_a * alpha2) to N / 2 columns.
-template <bool B_TERNARY, int OUT, int S, bool RES = false>
-__global__ void __launch_bounds__(S * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <bool B_TERNARY, int OUT, int S, bool RES = false, bool PAIR = false>
+__global__ void __launch_bounds__((PAIR ? 2 : S) * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__ a_sign,
                  const float* __restrict__ a_alpha, int64_t a_batch_rows,
                  const uint8_t* __restrict__ b_mask, const uint8_t* __restrict__ b_sign,
@@ -272,11 +276,16 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   int lin = blockIdx.x;
   if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
   lin += tile0;
-  const int band = lin / (kBand * tiles_n);
+  // PAIR: the order runs over column pairs; wave w takes column 2c + w (a
+  // missing last column repeats column tiles_n - 1 and stores nothing)
+  const int tn_order = PAIR ? (tiles_n + 1) / 2 : tiles_n;
+  const int band = lin / (kBand * tn_order);
   const int band_rows = min(kBand, tiles_m - band * kBand);
-  const int in_band = lin - band * kBand * tiles_n;
-  const int tile_n = in_band / band_rows;
-  const int tile_m = band * kBand + (in_band - tile_n * band_rows);
+  const int in_band = lin - band * kBand * tn_order;
+  const int tile_c = in_band / band_rows;
+  const int tile_m = band * kBand + (in_band - tile_c * band_rows);
+  const bool store_ok = !PAIR || 2 * tile_c + wid < tiles_n;
+  const int tile_n = PAIR ? min(2 * tile_c + wid, tiles_n - 1) : tile_c;
   const int64_t b = blockIdx.z;
   const int64_t m0 = (int64_t)tile_m * WAVE_TILE;
   const int64_t n0 = (int64_t)tile_n * WAVE_TILE;
@@ -292,17 +301,20 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
 
   const int64_t words = row_bytes / 8;          // 64-bit words per row
   const int64_t steps = (words + 3) / 4;        // 4 words (256 k) per step
-  const int64_t st0 = steps * wid / S;
-  const int64_t st1 = steps * (wid + 1) / S;
+  static_assert(!PAIR || S == 1, "paired waves each run the whole K range");
+  const int64_t st0 = PAIR ? 0 : steps * wid / S;
+  const int64_t st1 = PAIR ? steps : steps * (wid + 1) / S;
   constexpr int TPW = TILES / S;  // 32-row blocks of the tile each wave finally owns
-  const int rot = wid * TPW;      // acc[t] accumulates the tile's row block (t + rot) % 4
+  const int rot = PAIR ? 0 : wid * TPW;  // acc[t] accumulates the tile's row block (t + rot) % 4
 
-  // The tile's scales: wave 0 loads them first thing, the first DMAs go out
-  // behind them, and the wait for the first step (which completes them too)
-  // precedes their store to LDS, so their latency hides under the DMA's.
-  __shared__ float s_alpha_a[WAVE_TILE], s_alpha_b[WAVE_TILE];
+  // The tile's scales: wave 0 (PAIR: each wave, for its own columns; both store
+  // the same A scales) loads them first thing, the first DMAs go out behind
+  // them, and the wait for the first step (which completes them too) precedes
+  // their store to LDS, so their latency hides under the DMA's.
+  __shared__ float s_alpha_a[WAVE_TILE], s_alpha_b[PAIR ? 2 : 1][WAVE_TILE];
+  const int sw = PAIR ? wid : 0;
   float ra[WAVE_TILE / kWave], rbv[WAVE_TILE / kWave];
-  const bool scale_wave = OUT != (int)Elt::I32 && wid == 0;
+  const bool scale_wave = OUT != (int)Elt::I32 && (PAIR || wid == 0);
   if (scale_wave) {
 #pragma unroll
     for (int h = 0; h < WAVE_TILE / kWave; ++h) {
@@ -316,7 +328,7 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
 #pragma unroll
       for (int h = 0; h < WAVE_TILE / kWave; ++h) {
         s_alpha_a[h * kWave + lane] = ra[h];
-        s_alpha_b[h * kWave + lane] = rbv[h];
+        s_alpha_b[sw][h * kWave + lane] = rbv[h];
       }
     }
   };
@@ -328,10 +340,13 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  constexpr int SB = Stage<B_TERNARY>::kBytes;
-  constexpr int P = Stage<B_TERNARY>::kPlane;
-  constexpr int L = Stage<B_TERNARY>::kLoads;
-  uint8_t* ring = smem + (size_t)wid * kRing * SB;
+  constexpr int SB = Stage<B_TERNARY, PAIR>::kBytes;
+  constexpr int P = Stage<B_TERNARY, PAIR>::kPlane;
+  constexpr int L = Stage<B_TERNARY, PAIR>::kLoads;
+  uint8_t* ring = PAIR ? smem : smem + (size_t)wid * kRing * SB;
+  // plane offsets in a slot: A mask 0, A sign P, then this wave's B planes
+  const int bs_off = PAIR ? (2 + wid) * P : 2 * P;
+  const int bm_off = PAIR ? (4 + wid) * P : 3 * P;
   const uint32_t rb = (uint32_t)row_bytes;
   const bool straddle = (rb & 15u) == 8u;
   if (st0 < st1) {
@@ -356,8 +371,20 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
       }
     }
     // Descriptors stay plain locals (inside an aggregate they can land in VGPRs).
-    const __amdgpu_buffer_rsrc_t ram = uniform_rsrc(am), ras = uniform_rsrc(as), rbs = uniform_rsrc(bs);
+    const __amdgpu_buffer_rsrc_t ras = uniform_rsrc(as), rbs = uniform_rsrc(bs);
     const __amdgpu_buffer_rsrc_t rbm = B_TERNARY ? uniform_rsrc(bm) : rbs;
+    // PAIR: wave 0 loads the shared A mask plane, wave 1 the A sign plane
+    const __amdgpu_buffer_rsrc_t rao = uniform_rsrc(PAIR && wid ? as : am);
+    const int ao_off = PAIR ? wid * P : 0;
+    // PAIR: the other wave's DMAs of a step (and its reads of the slot about to
+    // be refilled) are done once both waves have passed their own wait
+    auto pair_sync = [&]() {
+      if constexpr (PAIR) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      }
+    };
     // Ring of 3 slots: step s0i + i lives in slot i % 3.  Steps past the wave's
     // range reload its last step (never used), which keeps the wait counts
     // uniform.  step_soff() picks the step (clamped) and returns its scalar
@@ -376,10 +403,10 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     };
     auto dma = [&](int st, uint8_t* slot) {  // all planes of one step
       const uint32_t so = step_soff(st);
-      dma_plane(ram, offa, so, slot);
-      dma_plane(ras, offa, so, slot + P);
-      dma_plane(rbs, offb, so, slot + 2 * P);
-      if constexpr (B_TERNARY) dma_plane(rbm, offb, so, slot + 3 * P);
+      dma_plane(rao, offa, so, slot + ao_off);
+      if constexpr (!PAIR) dma_plane(ras, offa, so, slot + P);
+      dma_plane(rbs, offb, so, slot + bs_off);
+      if constexpr (B_TERNARY) dma_plane(rbm, offb, so, slot + bm_off);
     };
     uint8_t* slot0 = ring;           // step st
     uint8_t* slot1 = ring + SB;      // step st + 1
@@ -399,18 +426,19 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     dma(s0i + 1, slot1);
     dma(s0i + 2, slot2);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * L));  // step st0 (and the scales) landed
+    pair_sync();
     store_scales();
     ready(s0i, slot0);
     read_words(na_m, slot0, r, g);
     read_words(na_s, slot0 + P, r, g);
     if constexpr (B_TERNARY) {
-      read_words(nb_s, slot0 + 2 * P, r, g);
-      read_words(nb_m, slot0 + 3 * P, r, g);
+      read_words(nb_s, slot0 + bs_off, r, g);
+      read_words(nb_m, slot0 + bm_off, r, g);
       prep_q01(nb_m, nb_s, qb01);
       prep_q23(nb_m, nb_s, qb23);
       ternary_slice(qb01, 0, ob[0]);
     } else {
-      read_words(wb, slot0 + 2 * P, r, g);
+      read_words(wb, slot0 + bs_off, r, g);
       binary_slice(wb, 0, ob[0]);
     }
     prep_q01(na_m, na_s, qa01);
@@ -444,13 +472,14 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     //   D: build slice 0 of step st + 1
     for (int st = s0i; st < s1i; ++st) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
+      pair_sync();
       ready(st + 1, slot1);
       const uint32_t so = step_soff(st + 3);
       read_words(na_m, slot1, r, g);
       read_words(na_s, slot1 + P, r, g);
       if constexpr (B_TERNARY) {
-        read_words(nb_s, slot1 + 2 * P, r, g);
-        read_words(nb_m, slot1 + 3 * P, r, g);
+        read_words(nb_s, slot1 + bs_off, r, g);
+        read_words(nb_m, slot1 + bm_off, r, g);
       }
       __builtin_amdgcn_sched_barrier(0);
       // A
@@ -461,7 +490,7 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
         binary_slice(wb, 1, ob[1]);
       prep_q01(na_m, na_s, qa01);
       if constexpr (B_TERNARY) prep_q01(nb_m, nb_s, qb01);
-      dma_plane(ram, offa, so, slot0);  // step st + 3 into the slot of step st
+      dma_plane(rao, offa, so, slot0 + ao_off);  // step st + 3 into the slot of step st
       BWTA_MFMA_SLICE(0);
       BWTA_REGION_END();
       // B
@@ -470,15 +499,15 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
         ternary_slice(qb23, 2, ob[0]);
       else
         binary_slice(wb, 2, ob[0]);
-      dma_plane(ras, offa, so, slot0 + P);
+      if constexpr (!PAIR) dma_plane(ras, offa, so, slot0 + P);
       BWTA_MFMA_SLICE(1);
       BWTA_REGION_END();
       // C
       read_words(na_m, slot1, r, g);
       read_words(na_s, slot1 + P, r, g);
       if constexpr (B_TERNARY) {
-        read_words(nb_s, slot1 + 2 * P, r, g);
-        read_words(nb_m, slot1 + 3 * P, r, g);
+        read_words(nb_s, slot1 + bs_off, r, g);
+        read_words(nb_m, slot1 + bm_off, r, g);
       }
       ternary_slice(qa23, 3, oa[1]);
       if constexpr (B_TERNARY)
@@ -489,8 +518,8 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
       if constexpr (B_TERNARY)
         prep_q23(nb_m, nb_s, qb23);
       else
-        read_words(wb, slot1 + 2 * P, r, g);
-      dma_plane(rbs, offb, so, slot0 + 2 * P);
+        read_words(wb, slot1 + bs_off, r, g);
+      dma_plane(rbs, offb, so, slot0 + bs_off);
       BWTA_MFMA_SLICE(0);
       BWTA_REGION_END();
       // D
@@ -499,7 +528,7 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
         ternary_slice(qb01, 0, ob[0]);
       else
         binary_slice(wb, 0, ob[0]);
-      if constexpr (B_TERNARY) dma_plane(rbm, offb, so, slot0 + 3 * P);
+      if constexpr (B_TERNARY) dma_plane(rbm, offb, so, slot0 + bm_off);
       BWTA_MFMA_SLICE(1);
       BWTA_REGION_END();
       uint8_t* const done = slot0;
@@ -569,6 +598,11 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  if (!store_ok) return;  // PAIR: the repeated last column
+  // Staging area of this wave's row blocks: its own ring, or (PAIR, one ring
+  // per block) its half of the block's ring, free once both waves are here.
+  uint8_t* const stg = PAIR ? smem + (size_t)wid * (WAVE_TILE * 4 + 16) * 32
+                            : smem + (size_t)wid * kRing * Stage<B_TERNARY>::kBytes;
 
   // Epilogue straight from the registers of the owned tile rows: y = acc *
   // (alpha_a[row] * alpha_b[col]) in fp32 (the product of the scales first),
@@ -586,7 +620,7 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     for (int qh = 0; qh < 4; ++qh) {
       float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       if constexpr (OUT != (int)Elt::I32)
-        v = *reinterpret_cast<const float4*>(&s_alpha_b[32 * j + 8 * qh + 4 * g]);
+        v = *reinterpret_cast<const float4*>(&s_alpha_b[sw][32 * j + 8 * qh + 4 * g]);
       ab[j][qh][0] = v.x;
       ab[j][qh][1] = v.y;
       ab[j][qh][2] = v.z;
@@ -632,7 +666,7 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
               o[jj][qh][u] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y);
           }
       if (full) {
-        store_row_block<TILES / 2, ES>(o, ring, r, g, lane, yrs, ldb, i);
+        store_row_block<TILES / 2, ES>(o, stg, r, g, lane, yrs, ldb, i);
       } else if (row < m_valid) {
 #pragma unroll
         for (int jj = 0; jj < TILES / 2; ++jj)
@@ -677,7 +711,7 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
             o[j][qh][u] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(a * (aa * ab[j][qh][u])));
         }
     if (full) {
-      store_row_block<TILES, ES>(o, ring, r, g, lane, yrs, ldb, i);
+      store_row_block<TILES, ES>(o, stg, r, g, lane, yrs, ldb, i);
     } else if (row < m_valid) {
 #pragma unroll
       for (int j = 0; j < TILES; ++j)
@@ -716,16 +750,18 @@ int choose_split(int64_t tiles, int64_t steps) {
   return best;
 }
 
-template <bool B_TERNARY, int OUT, int S, bool RES = false>
+// tiles: blocks of the launch (PAIR: column pairs, two waves each).
+template <bool B_TERNARY, int OUT, int S, bool RES = false, bool PAIR = false>
 hipError_t launch_k(const GemmArgs& g, int64_t row_bytes, int64_t tm, int64_t tn, int64_t tile0,
                     int64_t tiles, hipStream_t stream) {
-  size_t lds = (size_t)S * kRing * Stage<B_TERNARY>::kBytes;
+  size_t lds = (size_t)(PAIR ? 1 : S) * kRing * Stage<B_TERNARY, PAIR>::kBytes;
   if (S > 1 && lds < kXchgBytes) lds = kXchgBytes;
-  auto kfn = gemm_mfma_kernel<B_TERNARY, OUT, S, RES>;
+  auto kfn = gemm_mfma_kernel<B_TERNARY, OUT, S, RES, PAIR>;
   hipError_t e =
       hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kfn, dim3((unsigned)tiles, 1, (unsigned)g.batch), dim3(S * kWave), lds,
+  hipLaunchKernelGGL(kfn, dim3((unsigned)tiles, 1, (unsigned)g.batch),
+                     dim3((PAIR ? 2 : S) * kWave), lds,
                      stream, g.a_mask, g.a_sign, g.a_alpha, g.a_batch_rows, g.b_mask, g.b_sign,
                      g.b_alpha, g.b_batch_rows, g.M, g.N, row_bytes, (int)tm, (int)tn, g.Y, g.ldy,
                      g.y_batch_stride, (int)tile0);
@@ -771,6 +807,11 @@ hipError_t launch_plan(const GemmArgs& g, int64_t row_bytes, int64_t tm, int64_t
     if (e != hipSuccess) return e;
     return launch_s<B_TERNARY, OUT, RES>(g, 2, row_bytes, tm, tn, tiles - rem, rem, stream);
   }
+  // One unsplit launch: waves in pairs on adjacent column tiles, which load
+  // their shared A panel once (a third fewer L2 requests and LDS bytes).
+  if (tn >= 2)
+    return launch_k<B_TERNARY, OUT, 1, RES, true>(g, row_bytes, tm, tn, 0, tm * ((tn + 1) / 2),
+                                                  stream);
   return launch_s<B_TERNARY, OUT, RES>(g, 1, row_bytes, tm, tn, 0, tiles, stream);
 }
 

@@ -168,8 +168,13 @@ def test_gemm_ldy(bw, oracle):
 # launch.  Outputs start as a sentinel, every output is checked against the
 # properties |acc| <= nnz and acc = nnz (mod 2), and all rows against the oracle
 # on two columns of every 128-column tile.
+# Grids that stay one unsplit launch (a partial round above 512 tiles, or fewer
+# than 4 steps of K) run their waves in pairs on adjacent column tiles sharing A;
+# an odd column count leaves the last pair's second wave without a tile.
 GRID_SHAPES = [(2048, 8300, 1000),   # 16 x 65 tiles = 1024 + 16; ragged N, ragged K
-               (1900, 8960, 1536)]   # 15 x 70 tiles = 1024 + 26; ragged M
+               (1900, 8960, 1536),   # 15 x 70 tiles = 1024 + 26; ragged M
+               (1000, 24654, 300),   # 8 x 193 tiles = 1024 + 520: pairs, odd columns
+               (1100, 16500, 500)]   # 9 x 129 tiles, 2 steps of K: pairs, odd columns
 
 
 def _grid_columns(N, seed):
@@ -262,6 +267,27 @@ def test_batched_ternary_ternary(bw, oracle, H, L, D, algo):
     tk, _, _ = oracle.ternarize(k)
     for h in range(H):
         ref = oracle.matmul_i32(tq[h * L:(h + 1) * L], tk[h * L:(h + 1) * L])
+        assert (got[h] == ref).all(), f"head {h}"
+
+
+def test_batched_grid_pairs(bw, oracle):
+    """5 heads of L = 1913: 15 x 15 tiles per head, 1125 in all, so one unsplit
+    launch with paired waves and an odd column count; sentinel-filled output,
+    every score checked."""
+    import torch
+    H, L, D = 5, 1913, 128
+    rng = np.random.Generator(np.random.PCG64(H * L + D))
+    q = inputs.f32_to_bf16_bits(rng.standard_normal((H * L, D), dtype=np.float32))
+    k = inputs.f32_to_bf16_bits(rng.standard_normal((H * L, D), dtype=np.float32) * 1.5)
+    qa = bw.bwta_ternarize_pack(to_dev(q))
+    ka = bw.bwta_ternarize_pack(to_dev(k))
+    out = torch.full((H, L, L), 0x7FFFFFFF, dtype=torch.int32, device="cuda")
+    got = to_host(bw.bwta_batched_gemm(H, qa, L, ka, L, L, L, out_dtype="i32", algo="mfma",
+                                       out=out))
+    tq, _, _ = oracle.ternarize(q)
+    tk, _, _ = oracle.ternarize(k)
+    for h in range(H):
+        ref = oracle.matmul_i32(tq[h * L:(h + 1) * L], tk[h * L:(h + 1) * L], threads=8)
         assert (got[h] == ref).all(), f"head {h}"
 
 
