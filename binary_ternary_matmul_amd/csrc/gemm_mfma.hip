@@ -40,6 +40,11 @@
 //   slice 0 during slice 3, so the matrix cores never wait for a step boundary.
 // * K is split over S waves of one block (S in {1, 2, 4}) when the grid would
 //   otherwise leave SIMDs idle; the partial tiles are summed exactly in LDS.
+//   Grids of unsplit tiles can instead pair a block's two waves on adjacent
+//   column tiles that load their shared A panel once.
+// * Tiles go to the XCDs in bands of 8 tile rows, so each XCD's L2 holds a
+//   compact set of A and B panels; complete tiles store their output rows
+//   through LDS, whole rows per 16-byte store.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -269,8 +274,8 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   // contiguous run of that order, whose tiles then share A and B panels in the
   // XCD's L2.  Order: bands of kBand tile rows, column by column within a band,
   // so a run of r tiles spans about kBand rows and r / kBand columns (LLaMA-7B
-  // gate/up, 172 tiles per XCD: 1 MB of A and 1.4 MB of B panels, against 0.25 MB
-  // and all 5.6 MB of B for row-major runs).
+  // gate and up as separate products, 172 tiles per XCD: 1 MB of A and 1.4 MB of
+  // B panels, against 0.25 MB and all 5.6 MB of B for row-major runs).
   constexpr int kBand = 8;
   const int nblk = (int)gridDim.x;
   int lin = blockIdx.x;
@@ -787,7 +792,7 @@ hipError_t launch_s(const GemmArgs& g, int S, int64_t row_bytes, int64_t tm, int
 //   36.6 unsplit);
 // * otherwise whole rounds of 1024 unsplit tiles, and a last partial round of
 //   at most 512 tiles as a second launch with K split in two, which takes about
-//   half as long as a round (LLaMA-7B gate/up: 1024 + 352 tiles);
+//   half as long as a round (LLaMA-7B q/k/v stacked: 1024 + 512 tiles);
 // * batches and remainders above 512 unsplit: splitting every tile only adds
 //   exchange work there (gate/up 80 us unsplit, 84 / 118 us with S = 2 / 4 on
 //   every tile).
