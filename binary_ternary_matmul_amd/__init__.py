@@ -8,11 +8,12 @@ bit-packed binary/ternary MatMul for linear and attention operators).
 """
 from ._binding import (AttentionProbs, BinaryPlanes, BwtaError, ResidualPlanes, TernaryPlanes,
                        bwta_attention, bwta_batched_gemm, bwta_gemm, bwta_gemm_residual,
-                       bwta_gemv, bwta_gemv_residual, bwta_pack_weights, bwta_pack_weights_residual,
-                       bwta_ternarize_pack, lib, padded_k, row_bytes)
+                       bwta_gemm_workspace_size, bwta_gemv, bwta_gemv_residual,
+                       bwta_gemv_workspace_size, bwta_pack_weights, bwta_pack_weights_residual,
+                       bwta_ternarize_pack, lib, padded_k, row_bytes, workspace)
 
 __all__ = ["AttentionProbs", "BinaryPlanes", "BwtaError", "ResidualPlanes", "TernaryPlanes",
            "bwta_attention", "bwta_batched_gemm", "bwta_gemm", "bwta_gemm_residual",
-           "bwta_gemv_residual", "bwta_pack_weights_residual",
-           "bwta_gemv", "bwta_pack_weights", "bwta_ternarize_pack", "lib", "padded_k",
-           "row_bytes"]
+           "bwta_gemm_workspace_size", "bwta_gemv", "bwta_gemv_residual",
+           "bwta_gemv_workspace_size", "bwta_pack_weights", "bwta_pack_weights_residual",
+           "bwta_ternarize_pack", "lib", "padded_k", "row_bytes", "workspace"]

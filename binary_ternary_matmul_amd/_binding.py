@@ -56,11 +56,15 @@ def lib() -> ctypes.CDLL:
     L.bwta_pack_weights.argtypes = [P, I32, I64, I64, I64, I64, P, P, P]
     L.bwta_ternarize_pack.restype = I32
     L.bwta_ternarize_pack.argtypes = [P, I32, I64, I64, I64, P, P, P, P, P]
-    prod = [P, P, P, P, P, P, I64, I64, I64, P, I32, I64, I32, P]
+    SZ = ctypes.c_size_t
+    prod = [P, P, P, P, P, P, I64, I64, I64, P, I32, I64, I32, P, SZ, P]
     L.bwta_gemm.restype = I32
     L.bwta_gemm.argtypes = prod
     L.bwta_gemv.restype = I32
     L.bwta_gemv.argtypes = prod
+    for f in (L.bwta_gemm_workspace_size, L.bwta_gemv_workspace_size):
+        f.restype = SZ
+        f.argtypes = [I64, I64, I64, I32]
     L.bwta_batched_gemm.restype = I32
     L.bwta_batched_gemm.argtypes = [I64, P, P, P, P, I64, P, P, P, I64, I64, I64, I64, P, I32,
                                     I64, I64, I32, P]
@@ -122,6 +126,58 @@ def _dev_check(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be a device tensor")
 
 
+def _check_vec(t: Optional[torch.Tensor], n: int, dtype, name: str):
+    """A contiguous 1-D tensor of n elements of `dtype`."""
+    if t is None:
+        raise ValueError(f"{name} is missing")
+    if t.dtype != dtype or t.dim() != 1 or t.shape[0] != n or (n > 1 and t.stride(0) != 1):
+        raise ValueError(f"{name} must be a contiguous [{n}] {dtype} tensor "
+                         f"(got {tuple(t.shape)} {t.dtype})")
+
+
+def _check_plane(t: torch.Tensor, rows: int, K: int, name: str):
+    """A packed plane: uint8 [rows, row_bytes(K)] with rows packed back to back."""
+    rb = row_bytes(K)
+    if t.dtype != torch.uint8 or t.dim() != 2 or tuple(t.shape) != (rows, rb):
+        raise ValueError(f"{name} must be a uint8 [{rows}, {rb}] plane "
+                         f"(got {tuple(t.shape)} {t.dtype})")
+    if rows > 0 and (t.stride(1) != 1 or (rows > 1 and t.stride(0) != rb)):
+        raise ValueError(f"{name} must have strides ({rb}, 1) (got {t.stride()})")
+
+
+def _check_ternary(a: "TernaryPlanes", name: str) -> int:
+    """Check a ternary operand's planes, alpha and nnz; return its row count."""
+    rows = a.mask.shape[0] if a.mask.dim() == 2 else -1
+    _check_plane(a.mask, rows, a.K, f"{name}.mask")
+    _check_plane(a.sign, rows, a.K, f"{name}.sign")
+    _check_vec(a.alpha, rows, torch.float32, f"{name}.alpha")
+    _check_vec(a.nnz, rows, torch.int32, f"{name}.nnz")
+    return rows
+
+
+def _check_binary(w, rows_per_alpha: int, name: str) -> int:
+    """Check a binary operand (sign plane and alpha); return its plane row count."""
+    rows = w.sign.shape[0] if w.sign.dim() == 2 else -1
+    _check_plane(w.sign, rows, w.K, f"{name}.sign")
+    _check_vec(w.alpha, rows * rows_per_alpha, torch.float32, f"{name}.alpha")
+    return rows
+
+
+def _check_out(out: torch.Tensor, out_dtype: str, shape, device, name: str = "out"):
+    """The output: dtype `out_dtype`, `shape` (the last dimension may be a
+    prefix of a wider row), unit stride along its rows, on `device`."""
+    want = _OUT_TORCH[out_dtype]
+    if out.dtype != want:
+        raise ValueError(f"{name} has dtype {out.dtype} but out_dtype={out_dtype!r} "
+                         f"writes {want}")
+    if out.dim() != len(shape) or tuple(out.shape[:-1]) != tuple(shape[:-1]) or \
+            out.shape[-1] < shape[-1] or out.stride(-1) != 1:
+        raise ValueError(f"{name} must be {list(shape[:-1])} x >= {shape[-1]} with unit "
+                         f"stride along its rows (got {tuple(out.shape)}, {out.stride()})")
+    if out.device != device:
+        raise ValueError(f"{name} is on {out.device}, the operands on {device}")
+
+
 def bwta_pack_weights(W: torch.Tensor, transpose: bool = False) -> BinaryPlanes:
     """Binarize the rows of W [rows, K] (or its columns when transpose=True:
     W is then [K, rows] and column c becomes row c of the planes)."""
@@ -158,30 +214,91 @@ def bwta_ternarize_pack(X: torch.Tensor) -> TernaryPlanes:
     return TernaryPlanes(mask, sign, alpha, nnz, K)
 
 
+_WORKSPACE = {}  # device index -> zero-filled uint8 tensor (the "auto" workspaces)
+
+
+def workspace(device, nbytes: int) -> torch.Tensor:
+    """A zero-filled workspace of at least nbytes on `device`, shared by every
+    call that asks for "auto" (the library leaves its counters zero after each
+    call, so one buffer serves all calls on a stream).  Grown outside graph
+    capture only: warm a captured call up once first."""
+    dev = torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    ws = _WORKSPACE.get(idx)
+    if ws is None or ws.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("the shared workspace must grow, which cannot happen during "
+                               "graph capture: run the call once before capturing it")
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _WORKSPACE[idx] = ws
+    return ws
+
+
+def _workspace_arg(size_fn, M, N, K, algo, dev, ws):
+    """(pointer, bytes) of the workspace argument: None -> NULL (no split),
+    "auto" -> the shared buffer, a tensor -> that tensor."""
+    if ws is None:
+        return ctypes.c_void_p(0), 0
+    if isinstance(ws, str):
+        if ws != "auto":
+            raise ValueError(f"workspace must be None, 'auto' or a tensor (got {ws!r})")
+        need = int(size_fn(M, N, K, ALGOS[algo]))
+        if need == 0:
+            return ctypes.c_void_p(0), 0
+        ws = workspace(dev, need)
+    if ws.device != dev or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the operands' device")
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
 def _product(fn, name, a: TernaryPlanes, w: BinaryPlanes, out_dtype: str, algo: str,
-             out: Optional[torch.Tensor]):
+             out: Optional[torch.Tensor], ws="auto", size_fn=None):
     if a.K != w.K:
         raise ValueError(f"K mismatch: activations {a.K}, weights {w.K}")
-    M, N = a.mask.shape[0], w.sign.shape[0]
+    if out_dtype not in _OUT_TORCH or algo not in ALGOS:
+        raise ValueError(f"bad out_dtype {out_dtype!r} or algo {algo!r}")
+    M = _check_ternary(a, "a")
+    N = _check_binary(w, 1, "w")
+    dev = a.mask.device
     if out is None:
-        out = torch.empty((M, N), dtype=_OUT_TORCH[out_dtype], device=a.mask.device)
-    if out.dim() != 2 or out.shape[0] != M or out.shape[1] < N or out.stride(1) != 1:
-        raise ValueError("out must be [M, >=N] with unit column stride")
+        out = torch.empty((M, N), dtype=_OUT_TORCH[out_dtype], device=dev)
+    _check_out(out, out_dtype, (M, N), dev)
+    for t, n in ((a.sign, "a.sign"), (a.alpha, "a.alpha"), (a.nnz, "a.nnz"), (w.sign, "w.sign"),
+                 (w.alpha, "w.alpha")):
+        if t.device != dev:
+            raise ValueError(f"{n} is on {t.device}, a.mask on {dev}")
+    _dev_check(a.mask, "a.mask")
+    wp, wb = _workspace_arg(size_fn, M, N, a.K, algo, dev, ws)
     _check(fn(_ptr(a.mask), _ptr(a.sign), _ptr(a.alpha), _ptr(a.nnz), _ptr(w.sign), _ptr(w.alpha),
-              M, N, a.K, _ptr(out), DTYPES[out_dtype], out.stride(0), ALGOS[algo], _stream()), name)
+              M, N, a.K, _ptr(out), DTYPES[out_dtype], out.stride(0), ALGOS[algo], wp, wb,
+              _stream()), name)
     return out
 
 
 def bwta_gemm(a: TernaryPlanes, w: BinaryPlanes, out_dtype: str = "f32", algo: str = "auto",
-              out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y[M, N] = alpha_a * alpha_w * (t @ s^T) for the prefill linear."""
-    return _product(lib().bwta_gemm, "bwta_gemm", a, w, out_dtype, algo, out)
+              out: Optional[torch.Tensor] = None, workspace="auto") -> torch.Tensor:
+    """Y[M, N] = alpha_a * alpha_w * (t @ s^T) for the prefill linear.
+    workspace: None (no cross-block split), "auto" (a shared zero-filled buffer)
+    or a zero-initialised uint8 device tensor of bwta_gemm_workspace_size bytes."""
+    L = lib()
+    return _product(L.bwta_gemm, "bwta_gemm", a, w, out_dtype, algo, out, workspace,
+                    L.bwta_gemm_workspace_size)
 
 
 def bwta_gemv(a: TernaryPlanes, w: BinaryPlanes, out_dtype: str = "f32", algo: str = "auto",
-              out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Decode product for M <= 16 activation rows."""
-    return _product(lib().bwta_gemv, "bwta_gemv", a, w, out_dtype, algo, out)
+              out: Optional[torch.Tensor] = None, workspace="auto") -> torch.Tensor:
+    """Decode product for M <= 16 activation rows (workspace as for bwta_gemm)."""
+    L = lib()
+    return _product(L.bwta_gemv, "bwta_gemv", a, w, out_dtype, algo, out, workspace,
+                    L.bwta_gemv_workspace_size)
+
+
+def bwta_gemm_workspace_size(M: int, N: int, K: int, algo: str = "auto") -> int:
+    return int(lib().bwta_gemm_workspace_size(M, N, K, ALGOS[algo]))
+
+
+def bwta_gemv_workspace_size(M: int, N: int, K: int, algo: str = "auto") -> int:
+    return int(lib().bwta_gemv_workspace_size(M, N, K, ALGOS[algo]))
 
 
 def bwta_batched_gemm(batch: int, a: TernaryPlanes, a_batch_rows: int, b, b_batch_rows: int,
@@ -193,11 +310,27 @@ def bwta_batched_gemm(batch: int, a: TernaryPlanes, a_batch_rows: int, b, b_batc
     K = a.K
     if b.K != K:
         raise ValueError("K mismatch")
-    b_mask = b.mask if isinstance(b, TernaryPlanes) else None
+    if out_dtype not in _OUT_TORCH or algo not in ALGOS:
+        raise ValueError(f"bad out_dtype {out_dtype!r} or algo {algo!r}")
+    a_rows = _check_ternary(a, "a")
+    if isinstance(b, TernaryPlanes):
+        b_rows = _check_ternary(b, "b")
+        b_mask = b.mask
+    else:
+        b_rows = _check_binary(b, 1, "b")
+        b_mask = None
+    if batch > 0 and ((batch - 1) * a_batch_rows + M > a_rows or
+                      (batch - 1) * b_batch_rows + N > b_rows):
+        raise ValueError("the batch reaches past the rows of a or b")
+    dev = a.mask.device
     if out is None:
-        out = torch.empty((batch, M, N), dtype=_OUT_TORCH[out_dtype], device=a.mask.device)
-    if out.dim() != 3 or out.stride(2) != 1 or tuple(out.shape) != (batch, M, N):
+        out = torch.empty((batch, M, N), dtype=_OUT_TORCH[out_dtype], device=dev)
+    _check_out(out, out_dtype, (batch, M, N), dev)
+    if tuple(out.shape) != (batch, M, N):
         raise ValueError("out must be [batch, M, N] with unit column stride")
+    _dev_check(a.mask, "a.mask")
+    if b.sign.device != dev:
+        raise ValueError("a and b are on different devices")
     _check(lib().bwta_batched_gemm(batch, _ptr(a.mask), _ptr(a.sign), _ptr(a.alpha), _ptr(a.nnz),
                                    a_batch_rows, _ptr(b_mask), _ptr(b.sign), _ptr(b.alpha),
                                    b_batch_rows, M, N, K, _ptr(out), DTYPES[out_dtype],
@@ -223,21 +356,27 @@ def bwta_attention(q: TernaryPlanes, k: TernaryPlanes, v: BinaryPlanes, heads: i
     scale defaults to 1 / sqrt(D).  Returns O [heads, L, D], and with probs=True
     also the AttentionProbs the kernel computed on the way."""
     D = q.K
-    rows = q.mask.shape[0]
+    if out_dtype not in ("f32", "bf16"):
+        raise ValueError(f"bad out_dtype {out_dtype!r}")
+    rows = _check_ternary(q, "q")
     if heads <= 0 or rows % heads:
         raise ValueError("q rows must be heads * L")
     L = rows // heads
-    if k.K != D or k.mask.shape[0] != rows:
+    if k.K != D or _check_ternary(k, "k") != rows:
         raise ValueError("k must match q: [heads * L, D]")
-    if v.K != L or v.sign.shape[0] != heads * D:
+    if v.K != L or _check_binary(v, 1, "v") != heads * D:
         raise ValueError("v must be V^T planes [heads * D, L]")
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
     dev = q.mask.device
     if out is None:
         out = torch.empty((heads, L, D), dtype=_OUT_TORCH[out_dtype], device=dev)
+    _check_out(out, out_dtype, (heads, L, D), dev)
     if tuple(out.shape) != (heads, L, D) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [heads, L, D] tensor")
+    if k.mask.device != dev or v.sign.device != dev:
+        raise ValueError("q, k and v are on different devices")
+    _dev_check(q.mask, "q.mask")
     pr = None
     if probs:
         pr = AttentionProbs(torch.empty((rows, L), dtype=torch.float32, device=dev),
@@ -292,11 +431,20 @@ def _residual(fn, name, a: TernaryPlanes, w: ResidualPlanes, out_dtype: str,
               out: Optional[torch.Tensor]) -> torch.Tensor:
     if a.K != w.K:
         raise ValueError(f"K mismatch: activations {a.K}, weights {w.K}")
-    M, N = a.mask.shape[0], w.sign.shape[0] // 2
+    if out_dtype not in ("f32", "bf16"):
+        raise ValueError(f"bad out_dtype {out_dtype!r} (two-plane products are scaled)")
+    M = _check_ternary(a, "a")
+    N2 = _check_binary(w, 1, "w")
+    if N2 % 2:
+        raise ValueError("two-plane weights have an even number of plane rows")
+    N = N2 // 2
+    dev = a.mask.device
     if out is None:
-        out = torch.empty((M, N), dtype=_OUT_TORCH[out_dtype], device=a.mask.device)
-    if out.dim() != 2 or out.shape[0] != M or out.shape[1] < N or out.stride(1) != 1:
-        raise ValueError("out must be [M, >=N] with unit column stride")
+        out = torch.empty((M, N), dtype=_OUT_TORCH[out_dtype], device=dev)
+    _check_out(out, out_dtype, (M, N), dev)
+    if w.sign.device != dev:
+        raise ValueError("a and w are on different devices")
+    _dev_check(a.mask, "a.mask")
     _check(fn(_ptr(a.mask), _ptr(a.sign), _ptr(a.alpha), _ptr(a.nnz), _ptr(w.sign),
               _ptr(w.alpha), M, N, a.K, _ptr(out), DTYPES[out_dtype], out.stride(0), _stream()),
            name)

@@ -87,6 +87,29 @@ bwta_status check_product(const uint8_t* a_mask, const uint8_t* a_sign, const fl
   return BWTA_OK;
 }
 
+// Workspace bytes of one product call: the decode kernel's cross-block K split
+// is the only user.  gemv: the FP4 decode kernel (AUTO from two rows on, MFMA,
+// MFMA_I8); gemm: AUTO sends M <= 16 to the same decode kernels.
+size_t product_workspace(int64_t M, int64_t N, int64_t K, bwta_algo algo, bool gemv) {
+  if (M <= 0 || N <= 0 || K <= 0 || K > BWTA_MAX_K || M > 16) return 0;
+  bool fp4_decode;
+  if (gemv)
+    fp4_decode = algo == BWTA_ALGO_MFMA || algo == BWTA_ALGO_MFMA_I8 ||
+                 (algo == BWTA_ALGO_AUTO && M >= 2);
+  else
+    fp4_decode = algo == BWTA_ALGO_AUTO && M >= 2;
+  return fp4_decode ? bwta::gemv_mfma_workspace_bytes(M, N, K) : 0;
+}
+
+bwta_status check_workspace(const void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return BWTA_OK;  // no workspace: no cross-block split
+  if (!aligned(ws, 256)) return fail(BWTA_ERR_ALIGN, "workspace is not 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(BWTA_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu this call needs",
+                ws_bytes, need);
+  return BWTA_OK;
+}
+
 bwta::Elt elt(bwta_dtype d) {
   return d == BWTA_F32 ? bwta::Elt::F32 : d == BWTA_BF16 ? bwta::Elt::BF16 : bwta::Elt::I32;
 }
@@ -173,6 +196,9 @@ bwta_status bwta_ternarize_pack(const void* X, bwta_dtype x_dtype, int64_t rows,
 static bwta_status run_product(const bwta::GemmArgs& g, bwta_algo algo, bool gemv,
                                hipStream_t stream) {
   const int64_t row_bytes = (g.K + 63) / 64 * 8;
+  // A single (unbatched) product of at most 16 activation rows is a decode
+  // product: with AUTO, bwta_gemm runs it on the decode kernels as well.
+  if (!gemv && algo == BWTA_ALGO_AUTO && g.batch == 1 && !g.b_mask && g.M <= 16) gemv = true;
   if (algo == BWTA_ALGO_AUTO) {
     // Decode: a single activation row costs the popcount GEMV one merge and one
     // population count per weight word, less than building FP4 operands; from
@@ -202,15 +228,29 @@ static bwta_status run_product(const bwta::GemmArgs& g, bwta_algo algo, bool gem
   return from_hip(e, "product launch");
 }
 
+size_t bwta_gemm_workspace_size(int64_t M, int64_t N, int64_t K, bwta_algo algo) {
+  return product_workspace(M, N, K, algo, false);
+}
+
+size_t bwta_gemv_workspace_size(int64_t M, int64_t N, int64_t K, bwta_algo algo) {
+  return product_workspace(M, N, K, algo, true);
+}
+
 bwta_status bwta_gemm(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
                       const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha, int64_t M,
                       int64_t N, int64_t K, void* Y, bwta_dtype y_dtype, int64_t ldy,
-                      bwta_algo algo, void* stream) {
+                      bwta_algo algo, void* workspace, size_t ws_bytes, void* stream) {
   BWTA_TRY(check_product(a_mask, a_sign, a_alpha, a_nnz, nullptr, false, w_sign, w_alpha, M, N, K,
                          Y, y_dtype, ldy, algo));
   if (M == 0 || N == 0) return BWTA_OK;
+  const size_t need = product_workspace(M, N, K, algo, false);
+  BWTA_TRY(check_workspace(workspace, ws_bytes, need));
   bwta::GemmArgs g{a_mask, a_sign, a_alpha, a_nnz, 0, nullptr, w_sign, w_alpha, 0,
                    1, M, N, K, Y, elt(y_dtype), ldy, 0};
+  if (need > 0) {
+    g.ws = workspace;
+    g.ws_bytes = ws_bytes;
+  }
   return run_product(g, algo, false, static_cast<hipStream_t>(stream));
 }
 
@@ -278,13 +318,19 @@ bwta_status bwta_gemv_residual(const uint8_t* a_mask, const uint8_t* a_sign, con
 bwta_status bwta_gemv(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
                       const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha, int64_t M,
                       int64_t N, int64_t K, void* Y, bwta_dtype y_dtype, int64_t ldy,
-                      bwta_algo algo, void* stream) {
+                      bwta_algo algo, void* workspace, size_t ws_bytes, void* stream) {
   BWTA_TRY(check_product(a_mask, a_sign, a_alpha, a_nnz, nullptr, false, w_sign, w_alpha, M, N, K,
                          Y, y_dtype, ldy, algo));
   if (M > 16) return fail(BWTA_ERR_UNSUPPORTED, "bwta_gemv takes M <= 16 (got %lld)", (long long)M);
   if (M == 0 || N == 0) return BWTA_OK;
+  const size_t need = product_workspace(M, N, K, algo, true);
+  BWTA_TRY(check_workspace(workspace, ws_bytes, need));
   bwta::GemmArgs g{a_mask, a_sign, a_alpha, a_nnz, 0, nullptr, w_sign, w_alpha, 0,
                    1, M, N, K, Y, elt(y_dtype), ldy, 0};
+  if (need > 0) {
+    g.ws = workspace;
+    g.ws_bytes = ws_bytes;
+  }
   return run_product(g, algo, true, static_cast<hipStream_t>(stream));
 }
 

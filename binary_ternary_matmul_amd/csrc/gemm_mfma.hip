@@ -631,8 +631,11 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
       ab[j][qh][2] = v.z;
       ab[j][qh][3] = v.w;
     }
+  // The staged stores write 16 bytes at a time: they need a 16-byte aligned tile
+  // origin and row pitch (the C interface asks only for element alignment).
   const bool full = m_valid == WAVE_TILE && n_valid == WAVE_TILE &&
-                    (int64_t)WAVE_TILE * ldy * ES < (int64_t)0x7FFFFFFF;
+                    (int64_t)WAVE_TILE * ldy * ES < (int64_t)0x7FFFFFFF &&
+                    ((ldy * ES) & 15) == 0 && (reinterpret_cast<uintptr_t>(ytile) & 15) == 0;
   const __amdgpu_buffer_rsrc_t yrs = uniform_rsrc(ytile);
   const uint32_t ldb = (uint32_t)(ldy * ES);
   if constexpr (RES) {

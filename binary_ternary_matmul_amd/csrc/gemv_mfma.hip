@@ -140,12 +140,22 @@ __host__ __device__ inline LdsLayout lds_layout(bool expanded, int chunks, int M
 // many chunks per batch (the same bytes in flight), multiplies both by the same
 // activation operands, and the epilogue writes
 // y = (T - 2 U1) (alpha_a alpha1) + (T - 2 U2) (alpha_a alpha2).
-template <int S, bool X, int OUT, bool RES = false>
+//
+// XB: K split across blocks (a workspace is given).  blockIdx.y = ky picks the
+// block's contiguous chunk range, one of gridDim.y; the block stages only that
+// range, every wave (S = 1) multiplies its tile over it and stores the exact
+// int32 partial T_ky - 2 U_ky of its 16 x 16 outputs to the workspace, then
+// counts itself in the tile's arrival counter.  The last of the gridDim.y blocks
+// to arrive adds the partials (integers: the order does not matter), applies the
+// epilogue and returns the counter to zero, so no block ever waits for another.
+template <int S, bool X, int OUT, bool RES = false, bool XB = false>
 __global__ void __launch_bounds__(kMaxW * kWave)
 gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__ a_sign,
                  const float* __restrict__ a_alpha, int M, const uint8_t* __restrict__ w_sign,
                  const float* __restrict__ w_alpha, int64_t N, int row_bytes,
-                 void* __restrict__ Y, int64_t ldy) {
+                 void* __restrict__ Y, int64_t ldy, int* __restrict__ ws_ctr,
+                 int* __restrict__ ws_part) {
+  static_assert(!XB || (S == 1 && !RES), "the cross-block split runs unsplit one-plane waves");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int W = blockDim.x / kWave;
   const int R = W / S;  // row groups per block
@@ -162,9 +172,15 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   const int64_t p1 = RES ? 64 * (ot >> 1) + 16 * (ot & 1) : n0;  // its (first) plane rows
   const int64_t rows_left = N - n0;
   const int rows_here = rows_left <= 0 ? 0 : (rows_left < 16 ? (int)rows_left : 16);
-  const int chunks = (row_bytes + 63) / 64;
-  const int c0 = chunks * ks / S;
-  const int c1 = chunks * (ks + 1) / S;
+  // The block's chunk range [kc0, kc0 + chunks) (all of the row unless XB); LDS
+  // holds it at local chunk indices 0 .. chunks - 1.
+  const int all_chunks = (row_bytes + 63) / 64;
+  const int ky = XB ? (int)blockIdx.y : 0;
+  const int nsplit = XB ? (int)gridDim.y : 1;
+  const int kc0 = XB ? all_chunks * ky / nsplit : 0;
+  const int chunks = XB ? all_chunks * (ky + 1) / nsplit - kc0 : all_chunks;
+  const int c0 = kc0 + chunks * ks / S;
+  const int c1 = kc0 + chunks * (ks + 1) / S;
   const LdsLayout L = lds_layout(X, chunks, M, S, R, RES ? 2 : 1);
   int* tsum = reinterpret_cast<int*>(smem + L.t_off);
 
@@ -220,7 +236,7 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
       const int u = (int)threadIdx.x + k * (int)blockDim.x;
       int m, c, gg;
       unit_pos(u, m, c, gg);
-      const uint32_t off = u < units ? (uint32_t)(m * row_bytes + 64 * c + 16 * gg) : kOOB;
+      const uint32_t off = u < units ? (uint32_t)(m * row_bytes + 64 * (kc0 + c) + 16 * gg) : kOOB;
       sm[k] = __builtin_amdgcn_raw_buffer_load_b128(mrs, (int)off, 0, 0);
       ss[k] = __builtin_amdgcn_raw_buffer_load_b128(srs, (int)off, 0, 0);
     }
@@ -261,7 +277,7 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   auto stage_unit = [&](int u, v4u vm, v4u vs) {
     int m, c, gg;
     unit_pos(u, m, c, gg);
-    const int valid = row_bytes - 64 * c - 16 * gg;  // bytes of this unit inside the row
+    const int valid = row_bytes - 64 * (kc0 + c) - 16 * gg;  // bytes of this unit inside the row
     if (valid < 16) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
@@ -301,7 +317,7 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   for (int u = (int)threadIdx.x + kMaxSU * (int)blockDim.x; u < units; u += (int)blockDim.x) {
     int m, c, gg;
     unit_pos(u, m, c, gg);
-    const uint32_t off = (uint32_t)(m * row_bytes + 64 * c + 16 * gg);
+    const uint32_t off = (uint32_t)(m * row_bytes + 64 * (kc0 + c) + 16 * gg);
     stage_unit(u, __builtin_amdgcn_raw_buffer_load_b128(mrs, (int)off, 0, 0),
                __builtin_amdgcn_raw_buffer_load_b128(srs, (int)off, 0, 0));
   }
@@ -329,18 +345,19 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     for (int i = 0; i < PF; ++i) {
       const int c = cb + i;
       if (c < c1) {  // uniform
-        const uint32_t ao = am_base + (uint32_t)c * a_step;
+        const int cl = c - kc0;  // staged (local) chunk
+        const uint32_t ao = am_base + (uint32_t)cl * a_step;
         v4i bop[4];
         if constexpr (X) {
           // lane slot of chunk c (rows m >= M: the cleared extra chunk)
-          const uint32_t xo = live ? (uint32_t)c * 4096u +
-                                         (uint32_t)(g * 16 + (r ^ (((c & 1) << 2) | g))) * 16u
+          const uint32_t xo = live ? (uint32_t)cl * 4096u +
+                                         (uint32_t)(g * 16 + (r ^ (((cl & 1) << 2) | g))) * 16u
                                    : (uint32_t)chunks * 4096u;
 #pragma unroll
           for (int e = 0; e < 4; ++e) bop[e] = *reinterpret_cast<const v4i*>(smem + xo + e * 1024);
         } else {
           const v4u am = *reinterpret_cast<const v4u*>(smem + ao);
-          const v4u as = *reinterpret_cast<const v4u*>(smem + as_base + (uint32_t)c * a_step);
+          const v4u as = *reinterpret_cast<const v4u*>(smem + as_base + (uint32_t)cl * a_step);
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             uint32_t sl[4];
@@ -380,23 +397,22 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
 
   // 6. Epilogue.  Element u of the U tile in lane l: activation row m = l % 16,
   //    column n_base + 4 (l / 16) + u; the product is T[m] - 2U.
-  auto store = [&](int l, v4f u4, v4f u4b, int64_t nb) {
+  // emit: the products acc1 (and acc2, RES) of lane l's 4 outputs, exact
+  // integers in fp32, through the epilogue to Y.
+  auto emit = [&](int l, v4f acc1, v4f acc2v, int64_t nb) {
     const int m = l & 15;
     const int64_t n = nb + 4 * (l >> 4);
     if (m >= M || n >= N) return;
-    int tm = 0;
-    for (int w2 = 0; w2 < W; ++w2) tm += tsum[w2 * 16 + m];
-    const float t = (float)tm;
     uint32_t o[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float accf = t - 2.0f * u4[u];  // exact: integers below 2^24
+      const float accf = acc1[u];
       if constexpr (OUT == (int)Elt::I32) {
         o[u] = (uint32_t)(int)accf;
       } else {
         float y = accf * (aa * ab[u]);
         if constexpr (RES) {
-          const float y2 = (t - 2.0f * u4b[u]) * (aa * ab2[u]);
+          const float y2 = acc2v[u] * (aa * ab2[u]);
           y = y + y2;
         }
         o[u] = OUT == (int)Elt::F32 ? __float_as_uint(y)
@@ -420,8 +436,53 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
       }
     }
   };
+  // store: lane l's MFMA sums U (and U2) of the block's whole range, T - 2U.
+  auto store = [&](int l, v4f u4, v4f u4b, int64_t nb) {
+    const int m = l & 15;
+    int tm = 0;
+    for (int w2 = 0; w2 < W; ++w2) tm += tsum[w2 * 16 + m];
+    const float t = (float)tm;
+    v4f a1, a2;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a1[u] = t - 2.0f * u4[u];  // exact: integers below 2^24
+      a2[u] = t - 2.0f * u4b[u];
+    }
+    emit(l, a1, a2, nb);
+  };
 
-  if constexpr (S == 1) {
+  if constexpr (XB) {
+    if (rows_here > 0) {  // wave-uniform; tiles past N take no part in any split
+      const int m = lane & 15;
+      int tm = 0;
+      for (int w2 = 0; w2 < W; ++w2) tm += tsum[w2 * 16 + m];
+      v4i part;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) part[u] = tm - 2 * (int)acc[u];  // exact integers
+      const int64_t tiles_all = (N + 15) / 16;
+      *reinterpret_cast<v4i*>(ws_part + ((ky * tiles_all + ot) * kWave + lane) * 4) = part;
+      // Release this wave's partial device-wide, then count the block in.
+      __threadfence();
+      int old = 0;
+      if (lane == 0) old = atomicAdd(ws_ctr + ot, 1);
+      old = __shfl(old, 0, kWave);
+      if (old == nsplit - 1) {  // every other split has stored its partial
+        __threadfence();  // acquire: their partials are visible from here on
+        v4i sum = v4i{0, 0, 0, 0};
+        for (int k2 = 0; k2 < nsplit; ++k2) {
+          const v4i o2 = k2 == ky ? part
+                                  : *reinterpret_cast<const v4i*>(
+                                        ws_part + ((k2 * tiles_all + ot) * kWave + lane) * 4);
+          sum += o2;
+        }
+        if (lane == 0) ws_ctr[ot] = 0;  // the counter is zero again for the next call
+        v4f a1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a1[u] = (float)sum[u];  // |acc| <= K < 2^24: exact
+        emit(lane, a1, a1, n0);
+      }
+    }
+  } else if constexpr (S == 1) {
     if (rows_here > 0) store(lane, acc, acc2, n0);
   } else {
     // Cross-wave sum of the S partial tiles of each row group (and plane).
@@ -472,18 +533,65 @@ Geometry geometry(int64_t N, int64_t row_bytes, int64_t mg, int accs = 1) {
   return q;
 }
 
-template <int S, bool X, int OUT, bool RES = false>
+// The cross-block K split (XB).  Where the in-block plan splits K over S waves
+// (fewer than 1536 tiles), P blocks take contiguous chunk ranges instead, each
+// staging only its range (LLaMA2-70B down, K = 28672: 28 KiB of planes per block
+// at M = 16 instead of 112 KiB, and expanded B operands instead of raw words).
+// The workspace starts with a fixed region of kCtrBytes for the arrival
+// counters (one per tile, zero between calls), followed by P int32 partial
+// tiles of 16 x 16 per tile.  The counter region is the same for every shape:
+// partials never reach into it, so the counters of any later call, whatever its
+// tile count, start at zero.
+struct Split {
+  bool use = false;
+  int P = 1, R = 1;
+  bool X = false;
+  int64_t blocks = 0;
+  size_t lds = 0, ctr_bytes = 0, ws_bytes = 0;
+};
+
+constexpr int64_t kMaxSplitTiles = 4096;  // P x tiles: at most 4 MiB of partials
+constexpr size_t kCtrBytes = 8192;        // counters of up to 2048 tiles (P >= 2)
+
+Split split_plan(int64_t M, int64_t N, int64_t row_bytes) {
+  Split sp;
+  if (M < 1 || M > 16 || N >= ((int64_t)1 << 29)) return sp;
+  const Geometry q1 = geometry(N, row_bytes, M);
+  const int64_t tiles = (N + 15) / 16;
+  const int64_t chunks = (row_bytes + 63) / 64;
+  int P = q1.S;
+  while (P > 1 && tiles * P > kMaxSplitTiles) P /= 2;
+  if (P < 2 || tiles * 4 > (int64_t)kCtrBytes) return sp;
+  const int64_t cb = (chunks + P - 1) / P;  // the largest range
+  int64_t R = (tiles * P + 255) / 256;
+  if (R < 1) R = 1;
+  if (R > kMaxW) R = kMaxW;
+  sp.P = P;
+  sp.R = (int)R;
+  sp.blocks = (tiles + R - 1) / R;
+  sp.X = (size_t)lds_layout(true, (int)cb, (int)M, 1, sp.R).total <= kMaxLds;
+  sp.lds = lds_layout(sp.X, (int)cb, (int)M, 1, sp.R).total;
+  if (sp.lds > kMaxLds) return Split{};
+  sp.ctr_bytes = kCtrBytes;
+  sp.ws_bytes = sp.ctr_bytes + (size_t)P * (size_t)tiles * 1024;
+  sp.use = true;
+  return sp;
+}
+
+template <int S, bool X, int OUT, bool RES = false, bool XB = false>
 hipError_t launch_s(const GemmArgs& g, const Geometry& q, int64_t m0, int64_t mg,
-                    int64_t row_bytes, hipStream_t stream) {
-  auto kfn = gemv_mfma_kernel<S, X, OUT, RES>;
+                    int64_t row_bytes, hipStream_t stream, int splits = 1, int* ctr = nullptr,
+                    int* part = nullptr) {
+  auto kfn = gemv_mfma_kernel<S, X, OUT, RES, XB>;
   hipError_t e = hipFuncSetAttribute((const void*)kfn,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)q.lds);
   if (e != hipSuccess) return e;
   constexpr int ES = OUT == (int)Elt::BF16 ? 2 : 4;
-  hipLaunchKernelGGL(kfn, dim3((unsigned)q.blocks), dim3((unsigned)(q.S * q.R * kWave)), q.lds,
-                     stream, g.a_mask + m0 * row_bytes, g.a_sign + m0 * row_bytes,
+  hipLaunchKernelGGL(kfn, dim3((unsigned)q.blocks, (unsigned)splits),
+                     dim3((unsigned)(q.S * q.R * kWave)), q.lds, stream,
+                     g.a_mask + m0 * row_bytes, g.a_sign + m0 * row_bytes,
                      g.a_alpha ? g.a_alpha + m0 : nullptr, (int)mg, g.b_sign, g.b_alpha, g.N,
-                     (int)row_bytes, static_cast<char*>(g.Y) + m0 * g.ldy * ES, g.ldy);
+                     (int)row_bytes, static_cast<char*>(g.Y) + m0 * g.ldy * ES, g.ldy, ctr, part);
   return hipGetLastError();
 }
 
@@ -503,6 +611,25 @@ hipError_t launch_out(const GemmArgs& g, hipStream_t stream) {
   if ((RES ? 2 : 1) * g.N >= (int64_t)1 << 29) return hipErrorInvalidValue;  // 32-bit offsets
   const int64_t row_bytes = (g.K + 63) / 64 * 8;
   const int accs = RES ? 2 : 1;
+  if constexpr (!RES) {
+    const Split sp = g.ws ? split_plan(g.M, g.N, row_bytes) : Split{};
+    if (sp.use) {
+      if (g.ws_bytes < sp.ws_bytes) return hipErrorInvalidValue;  // checked by the caller
+      Geometry q;
+      q.S = 1;
+      q.R = sp.R;
+      q.X = sp.X;
+      q.blocks = sp.blocks;
+      q.lds = sp.lds;
+      q.fits = true;
+      int* ctr = static_cast<int*>(g.ws);
+      int* part = reinterpret_cast<int*>(static_cast<char*>(g.ws) + sp.ctr_bytes);
+      return sp.X ? launch_s<1, true, OUT, false, true>(g, q, 0, g.M, row_bytes, stream, sp.P,
+                                                        ctr, part)
+                  : launch_s<1, false, OUT, false, true>(g, q, 0, g.M, row_bytes, stream, sp.P,
+                                                         ctr, part);
+    }
+  }
   // Largest group of activation rows whose staging fits in LDS; one launch per
   // group.
   int64_t mg = g.M;
@@ -532,6 +659,11 @@ hipError_t launch_gemv_mfma_residual(const GemmArgs& g, hipStream_t stream) {
     default:
       return hipErrorInvalidValue;
   }
+}
+
+size_t gemv_mfma_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const Split sp = split_plan(M, N, (K + 63) / 64 * 8);
+  return sp.use ? sp.ws_bytes : 0;
 }
 
 hipError_t launch_gemv_mfma(const GemmArgs& g, hipStream_t stream) {

@@ -39,6 +39,10 @@ struct GemmArgs {
   void* Y;
   Elt y_dt;
   int64_t ldy, y_batch_stride;
+  // Optional workspace (zero-filled before its first use; every launch leaves
+  // its counters zero): enables the decode kernel's cross-block K split.
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
 };
 
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
@@ -52,6 +56,9 @@ hipError_t launch_gemv_popcount(const GemmArgs& g, hipStream_t stream);
 // Two-plane residual weights, M <= 16 (g.N outputs, 2 g.N interleaved plane rows).
 hipError_t launch_gemv_popcount_residual(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_gemv_mfma(const GemmArgs& g, hipStream_t stream);
+// Workspace bytes launch_gemv_mfma uses for this shape when one is given (0: the
+// shape runs without a cross-block split).
+size_t gemv_mfma_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // Two-plane residual weights, 2 <= M <= 16 (g.N outputs, 2 g.N interleaved plane rows).
 hipError_t launch_gemv_mfma_residual(const GemmArgs& g, hipStream_t stream);
 

@@ -200,6 +200,11 @@ pack_rows_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t sr, i
         if (lane == 0) red_sum[wid] = total;
         __syncthreads();
         total = tree16(&red_sum[row_in_block * W], W);
+        // The binary rule has no second barrier in this iteration: without this
+        // one a wave could store the next row's sum over red_sum while a slower
+        // wave of the same row still reads it.  (The ternary rule's second
+        // barrier below already separates the two.)
+        if constexpr (!TERNARY) __syncthreads();
       }
     } else {
       total = lanes_tree<LPR>(part[0]);

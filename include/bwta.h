@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define BWTA_API_VERSION 1
+#define BWTA_API_VERSION 2
 /* Largest K (reduction length) any call accepts. */
 #define BWTA_MAX_K 65536
 
@@ -142,17 +142,38 @@ bwta_status bwta_ternarize_pack(const void* X, bwta_dtype x_dtype, int64_t rows,
                                 int64_t stride_row, uint8_t* mask, uint8_t* sign, float* alpha,
                                 int32_t* nnz, void* stream);
 
+/* Workspace (bwta_gemm, bwta_gemv).  A product may split its K range across
+ * thread blocks; each block then writes an exact int32 partial of its outputs
+ * to the workspace and counts itself in a per-tile arrival counter there, and
+ * the last block of a tile adds the partials, applies the epilogue and sets the
+ * counter back to zero.  The decode kernel does so where it would otherwise
+ * split K inside a block (fewer than 1536 tiles of 16 weight rows, LLaMA2-70B
+ * down for example).
+ *   workspace = NULL: no cross-block split (ws_bytes is ignored); the result is
+ *     the same, bit for bit.
+ *   Otherwise: device memory owned by the caller, 256-byte aligned
+ *     (BWTA_ERR_ALIGN), at least the size query's bytes for the call's shape
+ *     and algo (BWTA_ERR_INVALID if smaller; a size of 0 means the call does
+ *     not use it).  It must be zero-filled once before its first use; every
+ *     call that completes leaves its counters zero again, so the same buffer
+ *     serves any later call of any shape.  Calls that share a workspace must
+ *     not run concurrently (calls on one stream never do). */
+size_t bwta_gemm_workspace_size(int64_t M, int64_t N, int64_t K, bwta_algo algo);
+size_t bwta_gemv_workspace_size(int64_t M, int64_t N, int64_t K, bwta_algo algo);
+
 /* Prefill linear (page: Abstract, binary/ternary MatMul for linear operators):
  * Y[m][n] = epilogue(sum_k t[m][k] * s[n][k]) for a ternary A [M x K] (a_mask,
  * a_sign, a_alpha, a_nnz as written by bwta_ternarize_pack) and a binary
  * W [N x K] (w_sign, w_alpha as written by bwta_pack_weights).
  * Y: M x N, row-major with leading dimension ldy >= N (elements), dtype
  *    BWTA_F32, BWTA_BF16 or BWTA_I32 (raw accumulators; a_alpha and w_alpha
- *    may then be NULL). */
+ *    may then be NULL).
+ * With BWTA_ALGO_AUTO a product of M <= 16 rows runs on the decode kernels of
+ * bwta_gemv.  workspace, ws_bytes: see "Workspace" above (NULL allowed). */
 bwta_status bwta_gemm(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
                       const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha,
                       int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype, int64_t ldy,
-                      bwta_algo algo, void* stream);
+                      bwta_algo algo, void* workspace, size_t ws_bytes, void* stream);
 
 /* Prefill linear with two-plane residual weights (w_sign, w_alpha as written by
  * bwta_pack_weights_residual for N weight rows, 2N plane rows):
@@ -182,11 +203,12 @@ bwta_status bwta_gemv_residual(const uint8_t* a_mask, const uint8_t* a_sign, con
 /* Decode GEMV / skinny GEMM, 1 <= M <= 16: the same product as bwta_gemm with
  * kernels that stream the packed weights from HBM once (page: Abstract, lower
  * memory footprint; the replies quoted on the page name prefill and decode as
- * the workloads).  M > 16 returns BWTA_ERR_UNSUPPORTED. */
+ * the workloads).  M > 16 returns BWTA_ERR_UNSUPPORTED.  workspace, ws_bytes:
+ * see "Workspace" above (NULL allowed). */
 bwta_status bwta_gemv(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
                       const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha,
                       int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype, int64_t ldy,
-                      bwta_algo algo, void* stream);
+                      bwta_algo algo, void* workspace, size_t ws_bytes, void* stream);
 
 /* Batched products for attention (page: Abstract, binary/ternary MatMul for
  * attention operators).  For b in [0, batch):

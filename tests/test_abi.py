@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_sizes(L):
-    assert L.bwta_version() == 1
+    assert L.bwta_version() == 2
     for K, kp in [(1, 64), (64, 64), (65, 128), (768, 768), (11008, 11008), (100, 128)]:
         assert L.bwta_padded_k(K) == kp
         assert L.bwta_row_bytes(K) == kp // 8
@@ -52,13 +52,14 @@ def test_status_strings(L):
 
 def gemm(L, fn="bwta_gemm", **kw):
     args = dict(a_mask=A, a_sign=A, a_alpha=A, a_nnz=A, w_sign=A, w_alpha=A, M=4, N=4, K=64,
-                Y=A, y_dtype=0, ldy=4, algo=0)
+                Y=A, y_dtype=0, ldy=4, algo=0, ws=0, ws_bytes=0)
     args.update(kw)
     f = getattr(L, fn)
     return f(*[ctypes.c_void_p(args[k]) if k in ("a_mask", "a_sign", "a_alpha", "a_nnz", "w_sign",
-                                                  "w_alpha", "Y") else args[k]
+                                                  "w_alpha", "Y", "ws") else args[k]
                for k in ["a_mask", "a_sign", "a_alpha", "a_nnz", "w_sign", "w_alpha", "M", "N",
-                         "K", "Y", "y_dtype", "ldy", "algo"]], ctypes.c_void_p(0))
+                         "K", "Y", "y_dtype", "ldy", "algo", "ws", "ws_bytes"]],
+             ctypes.c_void_p(0))
 
 
 @pytest.mark.parametrize("fn", ["bwta_gemm", "bwta_gemv"])
@@ -90,6 +91,38 @@ def test_product_validation(L, fn):
 def test_gemv_rejects_m_above_16(L):
     assert gemm(L, "bwta_gemv", M=17) == UNSUPPORTED
     assert b"16" in L.bwta_last_error()
+
+
+def test_workspace_size_query(L):
+    """The decode kernel splits K across blocks where it would otherwise split it
+    inside a block: LLaMA2-70B down (N = 8192, K = 28672) from two rows on, not
+    gate/up (1792 tiles of 16 rows) and not the M = 1 popcount kernel."""
+    gv, gm = L.bwta_gemv_workspace_size, L.bwta_gemm_workspace_size
+    AUTO, MFMA, POPC = 0, 1, 2
+    need = gv(16, 8192, 28672, AUTO)
+    assert need > 0 and need % 256 == 0
+    assert need >= 512 * 16 * 16 * 4 * 2          # at least two int32 partial tiles each
+    assert need <= (4 << 20) + (8 << 10)          # the stated cap on partials
+    assert gv(4, 8192, 28672, AUTO) == need       # one tile of 16 rows holds M <= 16
+    assert gv(16, 8192, 28672, MFMA) == need
+    assert gv(1, 8192, 28672, AUTO) == 0          # popcount GEMV
+    assert gv(1, 8192, 28672, MFMA) > 0           # M = 1 on the FP4 decode kernel
+    assert gv(16, 8192, 28672, POPC) == 0
+    assert gv(16, 28672, 8192, AUTO) == 0         # enough tiles: no split
+    assert gv(17, 8192, 28672, AUTO) == 0 and gv(0, 8192, 28672, AUTO) == 0
+    assert gm(16, 8192, 28672, AUTO) == need      # bwta_gemm AUTO routes M <= 16 here
+    assert gm(16, 8192, 28672, MFMA) == 0 and gm(64, 8192, 28672, AUTO) == 0
+
+
+@pytest.mark.parametrize("fn", ["bwta_gemm", "bwta_gemv"])
+def test_workspace_validation(L, fn):
+    shape = dict(M=16, N=8192, K=28672, ldy=8192)
+    need = getattr(L, fn + "_workspace_size")(16, 8192, 28672, 0)
+    assert gemm(L, fn, ws=A, ws_bytes=need - 1, **shape) == INVALID
+    assert b"workspace" in L.bwta_last_error()
+    assert gemm(L, fn, ws=A + 16, ws_bytes=need, **shape) == ALIGN
+    # a shape that does not use it ignores size and alignment
+    assert gemm(L, fn, ws=A + 16, ws_bytes=0, M=0) == OK
 
 
 def test_pack_validation(L):

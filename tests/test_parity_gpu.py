@@ -162,6 +162,27 @@ def test_gemm_ldy(bw, oracle):
         assert (o[:, :N] == ref["y"]).all() and (o[:, N:] == -7.0).all()
 
 
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_gemm_ldy_complete_tiles(bw, oracle, out_dtype):
+    """Complete 128 x 128 tiles (M, N multiples of 128) into rows whose pitch is
+    not a multiple of 16 bytes (ldy = 385): the tiles must not take the 16-byte
+    staged stores; every output and the gap columns are checked."""
+    import torch
+    M, N, K, ldy = 256, 384, 300, 385
+    x, w, ref = _linear_case(oracle, M, N, K)
+    a = bw.bwta_ternarize_pack(to_dev(x))
+    wp = bw.bwta_pack_weights(to_dev(w))
+    tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    for algo in ["mfma", "mfma_i8", "popcount"]:
+        out = torch.full((M, ldy), -7.0, dtype=tdt, device="cuda")
+        bw.bwta_gemm(a, wp, out_dtype=out_dtype, algo=algo, out=out[:, :N])
+        o = to_host(out)
+        want = oracle.to_bf16(ref["y"]) if out_dtype == "bf16" else ref["y"]
+        sentinel = to_host(torch.full((1,), -7.0, dtype=tdt))[0]
+        assert (o[:, :N].view(want.dtype) == want).all(), algo
+        assert (o[:, N:] == sentinel).all(), algo
+
 # Grids of more 128 x 128 output tiles than the chip's 1024 SIMDs: whole rounds
 # run one tile per wave over all of K, the last partial round (at most 512
 # tiles) splits each tile's K range over two waves, both kinds of blocks in one
@@ -209,34 +230,67 @@ def test_gemm_grid_rounds(bw, oracle, M, N, K):
     assert (yb[:, C] == oracle.to_bf16(ref)).all()
 
 
+@pytest.mark.parametrize("ws", [None, "auto"])
 @pytest.mark.parametrize("algo", ["popcount", "mfma", "mfma_i8", "auto"])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16])
 @pytest.mark.parametrize("N,K", [(1000, 1024), (513, 8192), (300, 28672), (77, 200)])
-def test_gemv(bw, oracle, M, N, K, algo):
+def test_gemv(bw, oracle, M, N, K, algo, ws):
+    """ws=None: no workspace (K split inside blocks); "auto": the shared
+    workspace, which splits K across blocks where 513 x 8192 and 300 x 28672
+    would split it inside a block."""
     x, w, ref = _linear_case(oracle, M, N, K, bf16=True)
     a = bw.bwta_ternarize_pack(to_dev(x))
     wp = bw.bwta_pack_weights(to_dev(w))
-    acc = to_host(bw.bwta_gemv(a, wp, out_dtype="i32", algo=algo))
+    acc = to_host(bw.bwta_gemv(a, wp, out_dtype="i32", algo=algo, workspace=ws))
     assert (acc == ref["acc"]).all()
-    y = to_host(bw.bwta_gemv(a, wp, out_dtype="f32", algo=algo))
+    y = to_host(bw.bwta_gemv(a, wp, out_dtype="f32", algo=algo, workspace=ws))
     assert (y.view(np.uint32) == ref["y"].view(np.uint32)).all()
 
 
+@pytest.mark.parametrize("ws", [None, "auto"])
 @pytest.mark.parametrize("algo", ["mfma", "popcount"])
 @pytest.mark.parametrize("M,N,K", [(16, 40, 65536), (13, 21, 40000), (9, 600, 36928),
                                    (16, 4100, 17000), (6, 33, 64), (2, 17, 129)])
-def test_gemv_launch_paths(bw, oracle, M, N, K, algo):
-    """Decode shapes that take the other launch paths of the FP4 GEMV: raw
-    activation planes (expanded operands do not fit in LDS), activation rows
-    split over several launches (K = 65536 at M = 16), a K split over up to 8
-    waves for few weight rows, ragged K and N, and tiny K."""
+def test_gemv_launch_paths(bw, oracle, M, N, K, algo, ws):
+    """Decode shapes that take the other launch paths of the FP4 GEMV.  Without
+    a workspace: raw activation planes (expanded operands do not fit in LDS),
+    activation rows split over several launches (K = 65536 at M = 16), a K split
+    over up to 8 waves for few weight rows, ragged K and N, and tiny K.  With
+    one, the in-block K splits become cross-block splits of up to 8 ranges."""
     x, w, ref = _linear_case(oracle, M, N, K, bf16=True)
     a = bw.bwta_ternarize_pack(to_dev(x))
     wp = bw.bwta_pack_weights(to_dev(w))
-    acc = to_host(bw.bwta_gemv(a, wp, out_dtype="i32", algo=algo))
+    acc = to_host(bw.bwta_gemv(a, wp, out_dtype="i32", algo=algo, workspace=ws))
     assert (acc == ref["acc"]).all()
-    y = to_host(bw.bwta_gemv(a, wp, out_dtype="bf16", algo=algo))
+    y = to_host(bw.bwta_gemv(a, wp, out_dtype="bf16", algo=algo, workspace=ws))
     assert (y == ref["y_bf16"]).all()
+
+
+def test_gemv_workspace_reuse(bw, oracle):
+    """One caller-owned workspace through several calls: the first shape (ragged
+    K = 28736, 57 chunks in 4 ranges) twice, then a smaller one, then bwta_gemm
+    (AUTO sends M <= 16 to the same kernel).  Every output is checked, and the
+    per-tile counters at the front of the workspace read zero after each call
+    (a later call with more tiles must not find an earlier call's partials where
+    its counters are)."""
+    import torch
+    cases = [(16, 1000, 28736), (16, 1000, 28736), (3, 300, 9000), (7, 513, 16384),
+             (16, 4100, 17000)]   # more tiles than any call before it
+    need = max(bw.bwta_gemv_workspace_size(M, N, K) for M, N, K in cases)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, (M, N, K) in enumerate(cases):
+        assert bw.bwta_gemv_workspace_size(M, N, K) > 0, (M, N, K)
+        x, w, ref = _linear_case(oracle, M, N, K, bf16=True)
+        a = bw.bwta_ternarize_pack(to_dev(x))
+        wp = bw.bwta_pack_weights(to_dev(w))
+        fn = bw.bwta_gemm if i >= 3 else bw.bwta_gemv
+        acc = to_host(fn(a, wp, out_dtype="i32", algo="auto", workspace=ws))
+        assert (acc == ref["acc"]).all(), f"call {i}: accumulators differ"
+        y = to_host(fn(a, wp, out_dtype="f32", algo="auto", workspace=ws))
+        assert (y.view(np.uint32) == ref["y"].view(np.uint32)).all(), f"call {i}: outputs differ"
+        tiles = (N + 15) // 16
+        assert (to_host(ws[:4 * tiles].view(torch.int32)) == 0).all(), f"call {i}: counters left"
 
 
 def test_gemv_ldy(bw, oracle):
@@ -290,6 +344,33 @@ def test_batched_grid_pairs(bw, oracle):
         ref = oracle.matmul_i32(tq[h * L:(h + 1) * L], tk[h * L:(h + 1) * L], threads=8)
         assert (got[h] == ref).all(), f"head {h}"
 
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_batched_grid_pairs_scaled(bw, oracle, out_dtype):
+    """The paired-wave grid of test_batched_grid_pairs (5 x 1913 x 1913, ternary
+    B, odd column count) with the scaled epilogue: each wave of a pair uses its
+    own column scales; every output compared bit for bit."""
+    import torch
+    H, L, D = 5, 1913, 128
+    rng = np.random.Generator(np.random.PCG64(H * L + D + 1))
+    q = inputs.f32_to_bf16_bits(rng.standard_normal((H * L, D), dtype=np.float32))
+    k = inputs.f32_to_bf16_bits(rng.standard_normal((H * L, D), dtype=np.float32) * 0.7)
+    qa = bw.bwta_ternarize_pack(to_dev(q))
+    ka = bw.bwta_ternarize_pack(to_dev(k))
+    tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out = torch.full((H, L, L), float("nan"), dtype=tdt, device="cuda")
+    got = to_host(bw.bwta_batched_gemm(H, qa, L, ka, L, L, L, out_dtype=out_dtype, algo="mfma",
+                                       out=out))
+    tq, aq, _ = oracle.ternarize(q)
+    tk, ak, _ = oracle.ternarize(k)
+    for h in range(H):
+        rows = slice(h * L, (h + 1) * L)
+        ref = oracle.scale(oracle.matmul_i32(tq[rows], tk[rows], threads=8), aq[rows], ak[rows])
+        if out_dtype == "bf16":
+            assert (got[h] == oracle.to_bf16(ref)).all(), f"head {h}"
+        else:
+            assert (got[h].view(np.uint32) == ref.view(np.uint32)).all(), f"head {h}"
 
 def test_pack_weights_columns_all_heads(bw, oracle):
     """V laid out [L, H*D]: one call packs V^T of every head (row h*D + d)."""
