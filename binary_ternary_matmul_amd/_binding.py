@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
     L.bwta_gemm.argtypes = prod
     L.bwta_gemv.restype = I32
     L.bwta_gemv.argtypes = prod
+    L.bwta_gemv_noalloc.restype = I32
+    L.bwta_gemv_noalloc.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, I32, I64, I32, P]
     for f in (L.bwta_gemm_workspace_size, L.bwta_gemv_workspace_size):
         f.restype = SZ
         f.argtypes = [I64, I64, I64, I32]
@@ -291,6 +293,19 @@ def bwta_gemv(a: TernaryPlanes, w: BinaryPlanes, out_dtype: str = "f32", algo: s
     L = lib()
     return _product(L.bwta_gemv, "bwta_gemv", a, w, out_dtype, algo, out, workspace,
                     L.bwta_gemv_workspace_size)
+
+
+def bwta_gemv_noalloc(a: TernaryPlanes, w: BinaryPlanes, out_dtype: str = "f32",
+                      algo: str = "auto", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bwta_gemv on the library's own scratch array instead of a workspace (for
+    callers that cannot allocate; pass `out` to allocate nothing here either)."""
+    return _product(_noalloc_shim, "bwta_gemv_noalloc", a, w, out_dtype, algo, out, None, None)
+
+
+def _noalloc_shim(*args):
+    # _product passes (..., algo, workspace, ws_bytes, stream); the entry point
+    # takes no workspace.
+    return lib().bwta_gemv_noalloc(*args[:13], args[15])
 
 
 def bwta_gemm_workspace_size(M: int, N: int, K: int, algo: str = "auto") -> int:

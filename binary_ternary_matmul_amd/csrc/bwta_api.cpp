@@ -334,6 +334,33 @@ bwta_status bwta_gemv(const uint8_t* a_mask, const uint8_t* a_sign, const float*
   return run_product(g, algo, true, static_cast<hipStream_t>(stream));
 }
 
+bwta_status bwta_gemv_noalloc(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
+                              const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha,
+                              int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype,
+                              int64_t ldy, bwta_algo algo, void* stream) {
+  BWTA_TRY(check_product(a_mask, a_sign, a_alpha, a_nnz, nullptr, false, w_sign, w_alpha, M, N, K,
+                         Y, y_dtype, ldy, algo));
+  if (M > 16)
+    return fail(BWTA_ERR_UNSUPPORTED, "bwta_gemv_noalloc takes M <= 16 (got %lld)", (long long)M);
+  if (M == 0 || N == 0) return BWTA_OK;
+  const size_t need = product_workspace(M, N, K, algo, true);
+  if (need > bwta::scratch_bytes())
+    return fail(BWTA_ERR_UNSUPPORTED,
+                "this shape needs %zu bytes of workspace, more than the %zu of the library's "
+                "scratch array", need, bwta::scratch_bytes());
+  bwta::GemmArgs g{a_mask, a_sign, a_alpha, a_nnz, 0, nullptr, w_sign, w_alpha, 0,
+                   1, M, N, K, Y, elt(y_dtype), ldy, 0};
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (need > 0) {
+    void* p = nullptr;
+    const hipError_t e = bwta::scratch_workspace(&p, st);
+    if (e != hipSuccess) return from_hip(e, "scratch array of bwta_gemv_noalloc");
+    g.ws = p;
+    g.ws_bytes = bwta::scratch_bytes();
+  }
+  return run_product(g, algo, true, st);
+}
+
 bwta_status bwta_batched_gemm(int64_t batch, const uint8_t* a_mask, const uint8_t* a_sign,
                               const float* a_alpha, const int32_t* a_nnz, int64_t a_batch_rows,
                               const uint8_t* b_mask, const uint8_t* b_sign, const float* b_alpha,

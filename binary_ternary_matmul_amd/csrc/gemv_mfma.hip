@@ -46,6 +46,8 @@
 //   weight stream.  S = 1: each lane applies y = (T - 2U) * (alpha_a[m] *
 //   alpha_w[n]) to its own 4 consecutive columns; S > 1: the partial tiles meet
 //   in LDS first.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -659,6 +661,62 @@ hipError_t launch_gemv_mfma_residual(const GemmArgs& g, hipStream_t stream) {
     default:
       return hipErrorInvalidValue;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Workspace of the allocation-free decode entry point (bwta_gemv_noalloc): one
+// file-scope array per GPU, large enough for every cross-block split plan
+// (the fixed counter region plus kMaxSplitTiles partial tiles).  Host code never
+// passes `scratch` itself to a kernel: it is a host-side stand-in, and the
+// device address of each GPU's copy comes from hipGetSymbolAddress, looked up
+// once per device with that device current.
+constexpr size_t kScratchBytes = kCtrBytes + (size_t)kMaxSplitTiles * 1024;
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+__global__ void __launch_bounds__(256) clear_words_kernel(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+bool g_scratch_done[kMaxDevices];
+
+}  // namespace
+
+size_t scratch_bytes() { return kScratchBytes; }
+
+hipError_t scratch_workspace(void** ptr, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_done[dev]) {
+    // First call on this device (which is current): the device address of its
+    // copy of the array, then one clear of the counter region on the caller's
+    // stream (a kernel, not a memset, so that the call may be captured in a
+    // graph).  Every later call finds the counters zero: each launch returns
+    // the ones it used to zero before it ends.
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e == hipSuccess) {
+      const int words = (int)(kCtrBytes / 4);
+      hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0,
+                         stream, static_cast<uint32_t*>(p), words);
+      e = hipGetLastError();
+    }
+    g_scratch_ptr[dev] = e == hipSuccess ? p : nullptr;
+    g_scratch_err[dev] = e;
+    g_scratch_done[dev] = true;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
 }
 
 size_t gemv_mfma_workspace_bytes(int64_t M, int64_t N, int64_t K) {

@@ -59,6 +59,11 @@ hipError_t launch_gemv_mfma(const GemmArgs& g, hipStream_t stream);
 // Workspace bytes launch_gemv_mfma uses for this shape when one is given (0: the
 // shape runs without a cross-block split).
 size_t gemv_mfma_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// The library's own per-GPU scratch array (bwta_gemv_noalloc): its size, and the
+// device address of the current device's copy (looked up, and its counter region
+// cleared on `stream`, on the first call per device).
+size_t scratch_bytes();
+hipError_t scratch_workspace(void** ptr, hipStream_t stream);
 // Two-plane residual weights, 2 <= M <= 16 (g.N outputs, 2 g.N interleaved plane rows).
 hipError_t launch_gemv_mfma_residual(const GemmArgs& g, hipStream_t stream);
 

@@ -210,6 +210,24 @@ bwta_status bwta_gemv(const uint8_t* a_mask, const uint8_t* a_sign, const float*
                       int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype, int64_t ldy,
                       bwta_algo algo, void* workspace, size_t ws_bytes, void* stream);
 
+/* bwta_gemv for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and result as bwta_gemv without the workspace: where bwta_gemv
+ * would use a workspace, this call uses the library's own scratch array, a
+ * file-scope device array of 4 MiB + 8 KiB of which every GPU the library runs
+ * on holds one copy until the process ends.  It allocates nothing (no hipMalloc,
+ * hipFree or allocating library call).  Shapes whose workspace would exceed the
+ * array return BWTA_ERR_UNSUPPORTED (no decode shape does: every split plan is
+ * capped at 4 MiB of partials).  The first call on a device looks up that
+ * device's copy and clears its counters with a small kernel on `stream`; every
+ * call leaves them zero.  All calls on one GPU share the array: calls that
+ * overlap in time on one GPU (different streams, different threads) race and
+ * may give wrong results; calls on one stream are ordered and safe. */
+bwta_status bwta_gemv_noalloc(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
+                              const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha,
+                              int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype,
+                              int64_t ldy, bwta_algo algo, void* stream);
+
 /* Batched products for attention (page: Abstract, binary/ternary MatMul for
  * attention operators).  For b in [0, batch):
  *   A_b = rows [b * a_batch_rows, b * a_batch_rows + M) of the ternary planes
