@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
     L.bwta_gemm.argtypes = prod
     L.bwta_gemv.restype = I32
     L.bwta_gemv.argtypes = prod
+    L.bwta_gemv_fused.restype = I32
+    L.bwta_gemv_fused.argtypes = [P, I32, I64, P, P, I64, I64, I64, P, I32, I64, P, P, P, P, P,
+                                  SZ, P]
     L.bwta_gemv_noalloc.restype = I32
     L.bwta_gemv_noalloc.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, I32, I64, I32, P]
     for f in (L.bwta_gemm_workspace_size, L.bwta_gemv_workspace_size):
@@ -293,6 +296,44 @@ def bwta_gemv(a: TernaryPlanes, w: BinaryPlanes, out_dtype: str = "f32", algo: s
     L = lib()
     return _product(L.bwta_gemv, "bwta_gemv", a, w, out_dtype, algo, out, workspace,
                     L.bwta_gemv_workspace_size)
+
+
+def bwta_gemv_fused(X: torch.Tensor, w: BinaryPlanes, out_dtype: str = "f32",
+                    out: Optional[torch.Tensor] = None, planes: bool = False,
+                    workspace="auto"):
+    """Decode linear in one launch: ternarize the rows of X [M, K] (fp32 or
+    bf16, unit stride along K, M <= 16) and multiply them with w.  Returns Y, or
+    (Y, TernaryPlanes) with planes=True (the kernel's ternarization of X)."""
+    if X.dtype not in (torch.float32, torch.bfloat16) or X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D float32/bfloat16 tensor with unit stride along K")
+    if out_dtype not in _OUT_TORCH:
+        raise ValueError(f"bad out_dtype {out_dtype!r}")
+    M, K = X.shape
+    if w.K != K:
+        raise ValueError(f"K mismatch: activations {K}, weights {w.K}")
+    N = _check_binary(w, 1, "w")
+    dev = X.device
+    if out is None:
+        out = torch.empty((M, N), dtype=_OUT_TORCH[out_dtype], device=dev)
+    _check_out(out, out_dtype, (M, N), dev)
+    if w.sign.device != dev:
+        raise ValueError("X and w are on different devices")
+    _dev_check(X, "X")
+    tp = None
+    if planes:
+        rb = row_bytes(K)
+        tp = TernaryPlanes(torch.empty((M, rb), dtype=torch.uint8, device=dev),
+                           torch.empty((M, rb), dtype=torch.uint8, device=dev),
+                           torch.empty(M, dtype=torch.float32, device=dev),
+                           torch.empty(M, dtype=torch.int32, device=dev), K)
+    L = lib()
+    wp, wb = _workspace_arg(L.bwta_gemv_workspace_size, M, N, K, "mfma", dev, workspace)
+    _check(L.bwta_gemv_fused(_ptr(X), _TORCH_DT[X.dtype], X.stride(0), _ptr(w.sign),
+                             _ptr(w.alpha), M, N, K, _ptr(out), DTYPES[out_dtype], out.stride(0),
+                             _ptr(tp.mask if tp else None), _ptr(tp.sign if tp else None),
+                             _ptr(tp.alpha if tp else None), _ptr(tp.nnz if tp else None), wp, wb,
+                             _stream()), "bwta_gemv_fused")
+    return (out, tp) if planes else out
 
 
 def bwta_gemv_noalloc(a: TernaryPlanes, w: BinaryPlanes, out_dtype: str = "f32",

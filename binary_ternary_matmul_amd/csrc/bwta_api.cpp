@@ -334,6 +334,50 @@ bwta_status bwta_gemv(const uint8_t* a_mask, const uint8_t* a_sign, const float*
   return run_product(g, algo, true, static_cast<hipStream_t>(stream));
 }
 
+bwta_status bwta_gemv_fused(const void* X, bwta_dtype x_dtype, int64_t ldx, const uint8_t* w_sign,
+                            const float* w_alpha, int64_t M, int64_t N, int64_t K, void* Y,
+                            bwta_dtype y_dtype, int64_t ldy, uint8_t* a_mask, uint8_t* a_sign,
+                            float* a_alpha, int32_t* a_nnz, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  if (!valid_io_dtype(x_dtype)) return fail(BWTA_ERR_INVALID, "bad activation dtype %d", (int)x_dtype);
+  if (M < 0 || N < 0) return fail(BWTA_ERR_INVALID, "negative size M=%lld N=%lld", (long long)M, (long long)N);
+  BWTA_TRY(check_k(K));
+  if (!valid_out_dtype(y_dtype)) return fail(BWTA_ERR_INVALID, "bad output dtype %d", (int)y_dtype);
+  if (ldy < N) return fail(BWTA_ERR_INVALID, "ldy (%lld) < N (%lld)", (long long)ldy, (long long)N);
+  if (ldx < K && M > 1) return fail(BWTA_ERR_INVALID, "ldx (%lld) < K (%lld)", (long long)ldx, (long long)K);
+  if (M > 16)
+    return fail(BWTA_ERR_UNSUPPORTED, "bwta_gemv_fused takes M <= 16 (got %lld)", (long long)M);
+  if (N >= ((int64_t)1 << 29)) return fail(BWTA_ERR_UNSUPPORTED, "N >= 2^29");
+  if ((a_mask == nullptr) != (a_sign == nullptr))
+    return fail(BWTA_ERR_INVALID, "a_mask and a_sign are given together or not at all");
+  if ((a_alpha == nullptr) != (a_nnz == nullptr))
+    return fail(BWTA_ERR_INVALID, "a_alpha and a_nnz are given together or not at all");
+  if (M == 0 || N == 0) return BWTA_OK;  // empty: pointers may be NULL
+  if (!X) return fail(BWTA_ERR_INVALID, "X is NULL");
+  if (!aligned(X, dtype_size(x_dtype))) return fail(BWTA_ERR_ALIGN, "X is not aligned to its element");
+  BWTA_TRY(check_plane(w_sign, "w_sign"));
+  BWTA_TRY(check_word(w_alpha, y_dtype != BWTA_I32, "w_alpha"));
+  if (!Y) return fail(BWTA_ERR_INVALID, "Y is NULL");
+  if (!aligned(Y, dtype_size(y_dtype))) return fail(BWTA_ERR_ALIGN, "Y is not aligned to its element");
+  if (a_mask) {
+    BWTA_TRY(check_plane(a_mask, "a_mask"));
+    BWTA_TRY(check_plane(a_sign, "a_sign"));
+  }
+  BWTA_TRY(check_word(a_alpha, false, "a_alpha"));
+  BWTA_TRY(check_word(a_nnz, false, "a_nnz"));
+  const size_t need = bwta::gemv_mfma_workspace_bytes(M, N, K);
+  BWTA_TRY(check_workspace(workspace, ws_bytes, need));
+  bwta::GemmArgs g{nullptr, nullptr, nullptr, nullptr, 0, nullptr, w_sign, w_alpha, 0,
+                   1, M, N, K, Y, elt(y_dtype), ldy, 0};
+  if (workspace && need > 0) {
+    g.ws = workspace;
+    g.ws_bytes = ws_bytes;
+  }
+  return from_hip(bwta::launch_gemv_fused(g, X, elt(x_dtype), ldx, a_mask, a_sign, a_alpha, a_nnz,
+                                          static_cast<hipStream_t>(stream)),
+                  "bwta_gemv_fused launch");
+}
+
 bwta_status bwta_gemv_noalloc(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,
                               const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha,
                               int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype,

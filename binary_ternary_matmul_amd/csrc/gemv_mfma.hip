@@ -78,6 +78,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t checked_rsrc(const void* base,
                                            0x00020000);
 }
 
+// s_waitcnt immediate for "vmcnt = 0" (expcnt and lgkmcnt at their no-wait
+// maxima; vmcnt is split over bits 3:0 and 15:14).
+constexpr int vmcnt_wait0() { return 0x0F70; }
+
 // Workgroup barrier that orders LDS only.  __syncthreads() also fences global
 // memory, which waits for every load in flight - here the whole weight stream.
 __device__ __forceinline__ void lds_barrier() {
@@ -136,6 +140,442 @@ __host__ __device__ inline LdsLayout lds_layout(bool expanded, int chunks, int M
   return l;
 }
 
+// ---------------------------------------------------------------------------
+// Fused ternarization (XT != 0): the block ternarizes its M activation rows
+// itself, from fp32 (XT = 1) or bf16 (XT = 2) values, by the rule of
+// bwta_ternarize_pack, and writes the packed bits straight into the raw staging
+// layout of its chunk range; so one launch does the decode linear's whole work.
+//
+// Reduction order.  With P the power of two at or above K, NT threads (a power
+// of two, NT <= blockDim) each own the aligned run [t V, t V + V) of V = P / NT
+// values (V >= 8, zeros past K).  A thread folds its run 8 values at a time into
+// a binary-counter stack (a perfect tree over the run), the 64 lanes of a wave
+// meet in a butterfly (lane bit 0 first) and the waves in a pairwise LDS tree, so
+// every total is the perfect pairwise tree over the zero-padded row, bit for bit.
+template <typename TX>
+struct XRun {
+  static constexpr int kWords = sizeof(TX) == 2 ? 4 : 8;  // 32-bit words per 8 values
+  static constexpr int kGroup = 16 / kWords;              // runs loaded per batch
+};
+
+__device__ __forceinline__ uint32_t x_bits(const uint32_t* w, int j, float) { return w[j]; }
+__device__ __forceinline__ uint32_t x_bits(const uint32_t* w, int j, uint16_t) {
+  return (w[j >> 1] >> (16 * (j & 1))) << 16;
+}
+
+template <typename TX>
+__device__ __forceinline__ void x_load_run(const TX* __restrict__ row, int64_t k0, int K, bool vec,
+                                           uint32_t (&w)[XRun<TX>::kWords]) {
+  constexpr int NW = XRun<TX>::kWords;
+  if (vec && k0 + 8 <= K) {
+#pragma unroll
+    for (int v = 0; v < NW / 4; ++v) {
+      const u32x4 u = *reinterpret_cast<const u32x4*>(row + k0 + v * (16 / (int)sizeof(TX)));
+#pragma unroll
+      for (int x = 0; x < 4; ++x) w[4 * v + x] = u[x];
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < NW; ++x) w[x] = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (k0 + j < K) {
+        uint32_t b;
+        if constexpr (sizeof(TX) == 4)
+          b = __float_as_uint(row[k0 + j]);
+        else
+          b = (uint32_t)row[k0 + j];
+        if constexpr (sizeof(TX) == 4)
+          w[j] = b;
+        else
+          w[j >> 1] |= b << (16 * (j & 1));
+      }
+    }
+  }
+}
+
+// Binary-counter merge of run n's tree node into the stack (levels 0..kXStack-1).
+// A thread folds at most 128 runs (V <= 1024 values: P <= 65536 over NT >= 64
+// threads, or P < 512), so 9 levels suffice.
+constexpr int kXStack = 9;
+__device__ __forceinline__ void stack_push(float (&st)[kXStack], int n, float node) {
+  bool open = true;
+#pragma unroll
+  for (int l = 0; l < kXStack; ++l) {
+    const bool merge = open && ((n >> l) & 1);
+    if (merge) node = st[l] + node;
+    if (open && !merge) {
+      st[l] = node;
+      open = false;
+    }
+  }
+}
+__device__ __forceinline__ float stack_root(const float (&st)[kXStack], int runs) {
+  float root = 0.0f;
+#pragma unroll
+  for (int l = 0; l < kXStack; ++l)
+    if ((runs >> l) & 1) root = st[l] + root;
+  return root;
+}
+
+// Sum over the NT participating threads: butterfly inside each wave, then the
+// pairwise tree over the waves' sums through `red` (NT / 64 entries, at most 8).
+__device__ __forceinline__ float block_tree(float v, int NT, float* red) {
+  const int lane = __lane_id();
+  const int wid = threadIdx.x / kWave;
+  const int lanes = NT < kWave ? NT : kWave;
+#pragma unroll
+  for (int b = 0; b < 6; ++b)
+    if ((1 << b) < lanes) v = v + __shfl_xor(v, 1 << b, kWave);
+  const int nw = NT < kWave ? 1 : NT / kWave;
+  if (lane == 0 && wid < nw) red[wid] = v;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  return tree16(red, nw);
+}
+__device__ __forceinline__ int block_isum(int v, int NT, int* red) {
+  const int lane = __lane_id();
+  const int wid = threadIdx.x / kWave;
+  const int lanes = NT < kWave ? NT : kWave;
+#pragma unroll
+  for (int b = 0; b < 6; ++b)
+    if ((1 << b) < lanes) v += __shfl_xor(v, 1 << b, kWave);
+  const int nw = NT < kWave ? 1 : NT / kWave;
+  if (lane == 0 && wid < nw) red[wid] = v;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  int s = 0;
+  for (int w = 0; w < nw; ++w) s += red[w];
+  return s;
+}
+
+// Fallback for rows whose run of values per thread does not fit the register
+// budget of fused_ternarize: one row at a time, the values read twice.
+template <typename TX>
+__device__ __forceinline__ void fused_ternarize_rows(const TX* __restrict__ X, int64_t ldx, int M, int K, int row_bytes,
+                                int kc0, int chunks, uint8_t* smem, uint32_t plane_bytes,
+                                int* tw, float* s_alpha, int* s_nnz, float* red, int* ired,
+                                uint8_t* o_mask, uint8_t* o_sign, float* o_alpha, int32_t* o_nnz,
+                                bool out_planes, bool out_scales) {
+  constexpr int NW = XRun<TX>::kWords, NG = XRun<TX>::kGroup;
+  int P = 1;
+  while (P < K) P <<= 1;
+  int Bp = 1;
+  while (2 * Bp <= (int)blockDim.x) Bp <<= 1;
+  const int NT = Bp < (P >= 8 ? P / 8 : 1) ? Bp : (P >= 8 ? P / 8 : 1);
+  const int V = P / NT;       // values per thread (>= 8 unless P < 8)
+  const int runs = (V + 7) / 8;
+  const int t = threadIdx.x;
+  const bool part = t < NT;
+  const int64_t kt = (int64_t)t * V;  // first value of the thread's run
+  const bool vec = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && ((ldx * (int64_t)sizeof(TX)) % 16 == 0) &&
+                   (K % 8 == 0);
+  const int lo = kc0 * 512, hi = (kc0 + chunks) * 512;  // the block's k range
+  for (int m = 0; m < M; ++m) {
+    const TX* row = X + (int64_t)m * ldx;
+    // pass 1: tree(|x|)
+    float st[kXStack];
+#pragma unroll
+    for (int l = 0; l < kXStack; ++l) st[l] = 0.0f;
+    for (int g0 = 0; g0 < runs; g0 += NG) {
+      uint32_t w[NG][NW];
+#pragma unroll
+      for (int i = 0; i < NG; ++i)
+        if (part && g0 + i < runs && kt + 8 * (g0 + i) < K)
+          x_load_run<TX>(row, kt + 8 * (g0 + i), K, vec, w[i]);
+        else
+#pragma unroll
+          for (int x = 0; x < NW; ++x) w[i][x] = 0u;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        if (g0 + i < runs) {
+          float a[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a[j] = __uint_as_float(x_bits(w[i], j, TX{}) & 0x7FFFFFFFu);
+          stack_push(st, g0 + i, lane_tree<8>(a));
+        }
+      }
+    }
+    const float total = block_tree(part ? stack_root(st, runs) : 0.0f, NT, red);
+    const float mu = total / (float)K;
+    const uint32_t uthr = __float_as_uint(0.5f * mu);
+    // pass 2: threshold, bits, tree(kept |x|), counts
+#pragma unroll
+    for (int l = 0; l < kXStack; ++l) st[l] = 0.0f;
+    int cnt = 0, tpart = 0;
+    for (int g0 = 0; g0 < runs; g0 += NG) {
+      uint32_t w[NG][NW];
+#pragma unroll
+      for (int i = 0; i < NG; ++i)
+        if (part && g0 + i < runs && kt + 8 * (g0 + i) < K)
+          x_load_run<TX>(row, kt + 8 * (g0 + i), K, vec, w[i]);
+        else
+#pragma unroll
+          for (int x = 0; x < NW; ++x) w[i][x] = 0u;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        if (g0 + i < runs) {
+          float kept[8];
+          uint32_t mb = 0, sb = 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t ux = x_bits(w[i], j, TX{});
+            const uint32_t ua = ux & 0x7FFFFFFFu;
+            const uint32_t keep = (uthr - ua) >> 31;  // |x| > thr (non-negative bit patterns)
+            kept[j] = __uint_as_float(ua & (0u - keep));
+            mb |= keep << j;
+            sb |= (keep & (ux >> 31)) << j;
+          }
+          stack_push(st, g0 + i, lane_tree<8>(kept));
+          const int64_t k0 = kt + 8 * (g0 + i);
+          cnt += __builtin_popcount(mb);
+          if (part && k0 >= lo && k0 < hi && k0 < (int64_t)row_bytes * 8) {
+            const int kl = (int)k0 - lo;  // local bit offset
+            const int cl = kl >> 9, gg = (kl >> 7) & 3, byte = (kl & 127) >> 3;
+            const uint32_t off = (uint32_t)(((cl * 4 + gg) * M + m) * 16 + byte);
+            smem[off] = (uint8_t)mb;
+            smem[plane_bytes + off] = (uint8_t)sb;
+            tpart += __builtin_popcount(mb) - 2 * __builtin_popcount(sb);
+            if (out_planes) {
+              o_mask[(int64_t)m * row_bytes + (k0 >> 3)] = (uint8_t)mb;
+              o_sign[(int64_t)m * row_bytes + (k0 >> 3)] = (uint8_t)sb;
+            }
+          }
+        }
+      }
+    }
+    if (tpart) atomicAdd(&tw[m], tpart);
+    // Rows shorter than 32 values: the runs cover bytes [0, (P + 7) / 8) of the
+    // 8-byte row; the rest of the plane row is zero padding.
+    if (out_planes && t == 0)
+      for (int b = (P + 7) / 8; b < row_bytes && b < hi / 8; ++b) {
+        o_mask[(int64_t)m * row_bytes + b] = 0;
+        o_sign[(int64_t)m * row_bytes + b] = 0;
+      }
+    const float ktot = block_tree(part ? stack_root(st, runs) : 0.0f, NT, red + 8);
+    const int ctot = block_isum(part ? cnt : 0, NT, ired);
+    const float alpha = ctot ? ktot / (float)ctot : 0.0f;
+    if (t == 0) {
+      s_alpha[m] = alpha;
+      s_nnz[m] = ctot;
+      if (out_scales) {
+        o_alpha[m] = alpha;
+        o_nnz[m] = ctot;
+      }
+    }
+  }
+}
+
+// The prologue.  Rows m < M of X (row m at X + m * ldx) become the raw staging
+// planes of local chunks [0, chunks) = global chunks [kc0, kc0 + chunks) (the
+// caller cleared them), the row sums T of that range go to the wave counters
+// tw (atomic adds), and alpha_a / nnz of the whole row to s_alpha / s_nnz.  With
+// out_planes the block also writes the planes of its range (and, with
+// out_scales, alpha and nnz) to global memory.
+//
+// Rows go in groups of G whose runs all fit 8 register slots per thread (slot i
+// holds run i % runs of row i / runs): one round of loads per group, the run
+// trees of each row added pairwise in registers (runs is a power of two, so
+// the row's slots form one aligned sub-tree), one butterfly per row, and two
+// block barriers per group.  red, red2, ired hold 16 rows x 8 waves each.
+template <typename TX>
+__device__ __forceinline__ void fused_ternarize(const TX* __restrict__ X, int64_t ldx, int M, int K,
+                                                int row_bytes, int kc0, int chunks, uint8_t* smem,
+                                                uint32_t plane_bytes, int* tw, float* s_alpha,
+                                                int* s_nnz, float* red, float* red2, int* ired,
+                                                uint8_t* o_mask, uint8_t* o_sign, float* o_alpha,
+                                                int32_t* o_nnz, bool out_planes, bool out_scales) {
+  constexpr int NW = XRun<TX>::kWords;
+  constexpr int SLOTS = 8;  // runs held at once (32 registers of bf16, 64 of fp32)
+  int P = 1;
+  while (P < K) P <<= 1;
+  int Bp = 1;
+  while (2 * Bp <= (int)blockDim.x) Bp <<= 1;
+  const int NT = Bp < (P >= 8 ? P / 8 : 1) ? Bp : (P >= 8 ? P / 8 : 1);
+  const int V = P / NT;
+  const int runs = (V + 7) / 8;  // a power of two
+  const int t = threadIdx.x;
+  if (t < 16) s_alpha[t] = 0.0f;  // rows m >= M read 0 (ordered by the barriers below)
+  // Vector loads only (16-byte aligned rows, K a multiple of 8), and the runs of
+  // a row within the slots; other inputs take the per-row fallback.
+  const bool vec = (reinterpret_cast<uintptr_t>(X) % 16 == 0) &&
+                   ((ldx * (int64_t)sizeof(TX)) % 16 == 0) && (K % 8 == 0);
+  if (runs > SLOTS || !vec) {
+    fused_ternarize_rows<TX>(X, ldx, M, K, row_bytes, kc0, chunks, smem, plane_bytes, tw, s_alpha,
+                             s_nnz, red, ired, o_mask, o_sign, o_alpha, o_nnz, out_planes,
+                             out_scales);
+    return;
+  }
+  const int lane = __lane_id();
+  const int wid = t / kWave;
+  const bool part = t < NT;
+  const int nw = NT < kWave ? 1 : NT / kWave;
+  const int lanes = NT < kWave ? NT : kWave;
+  const int64_t kt = (int64_t)t * V;
+  const int lo = kc0 * 512, hi = (kc0 + chunks) * 512;
+  const int G = SLOTS / runs;
+  const int lr = 31 - __builtin_clz(runs);  // runs = 2^lr: slot i is run i & (runs - 1) of row i >> lr
+  auto barrier = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  auto butterfly = [&](float v) {
+#pragma unroll
+    for (int b = 0; b < 6; ++b)
+      if ((1 << b) < lanes) v = v + __shfl_xor(v, 1 << b, kWave);
+    return v;
+  };
+  for (int m0 = 0; m0 < M; m0 += G) {
+    const int gm = M - m0 < G ? M - m0 : G;  // rows in this group
+    uint32_t w[SLOTS][NW];
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      const int gi = i >> lr, r = i & (runs - 1);
+      const int64_t k0 = kt + 8 * r;
+      if (part && gi < gm && k0 < K) {
+        const TX* src = X + (int64_t)(m0 + gi) * ldx + k0;
+#pragma unroll
+        for (int v = 0; v < NW / 4; ++v) {
+          const u32x4 u = *reinterpret_cast<const u32x4*>(src + v * (16 / (int)sizeof(TX)));
+#pragma unroll
+          for (int x = 0; x < 4; ++x) w[i][4 * v + x] = u[x];
+        }
+      } else {
+#pragma unroll
+        for (int x = 0; x < NW; ++x) w[i][x] = 0u;
+      }
+    }
+    // pass 1: |x| run trees, then pairwise over each row's runs
+    float n[SLOTS];
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      float a[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a[j] = __uint_as_float(x_bits(w[i], j, TX{}) & 0x7FFFFFFFu);
+      n[i] = lane_tree<8>(a);
+    }
+#pragma unroll
+    for (int h = 1; h < SLOTS; h <<= 1)
+      if (2 * h <= runs)
+#pragma unroll
+        for (int i = 0; i + h < SLOTS; i += 2 * h) n[i] = n[i] + n[i + h];
+#pragma unroll
+    for (int i = 0; i < SLOTS; i += 1) {
+      if ((i & (runs - 1)) == 0 && (i >> lr) < gm) {
+        const float v = butterfly(part ? n[i] : 0.0f);
+        if (lane == 0 && wid < nw) red[(i >> lr) * 8 + wid] = v;
+      }
+    }
+    barrier();
+    // the rows' thresholds, each computed once
+    uint32_t thr_g[SLOTS];
+#pragma unroll
+    for (int g = 0; g < SLOTS; ++g)
+      thr_g[g] = g < gm ? __float_as_uint(0.5f * (tree16(red + g * 8, nw) / (float)K)) : 0u;
+    // pass 2 (values still in registers): threshold, bits, kept trees, counts
+    float kn[SLOTS];
+    int cnt[SLOTS], tpart[SLOTS];
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      const int gi = i >> lr, r = i & (runs - 1);
+      const int m = m0 + gi;
+      kn[i] = 0.0f;
+      cnt[i] = 0;
+      tpart[i] = 0;
+      if (gi < gm) {
+        uint32_t uthr = thr_g[0];
+#pragma unroll
+        for (int g = 1; g <= i; ++g) uthr = gi == g ? thr_g[g] : uthr;
+        float kept[8];
+        uint32_t mb = 0, sb = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t ux = x_bits(w[i], j, TX{});
+          const uint32_t ua = ux & 0x7FFFFFFFu;
+          const uint32_t keep = (uthr - ua) >> 31;  // |x| > thr (non-negative bit patterns)
+          kept[j] = __uint_as_float(ua & (0u - keep));
+          mb |= keep << j;
+          sb |= (keep & (ux >> 31)) << j;
+        }
+        kn[i] = lane_tree<8>(kept);
+        cnt[i] = __builtin_popcount(mb);
+        const int64_t k0 = kt + 8 * r;
+        if (part && k0 >= lo && k0 < hi && k0 < (int64_t)row_bytes * 8) {
+          const int kl = (int)k0 - lo;
+          const int cl = kl >> 9, gg = (kl >> 7) & 3, byte = (kl & 127) >> 3;
+          const uint32_t off = (uint32_t)(((cl * 4 + gg) * M + m) * 16 + byte);
+          smem[off] = (uint8_t)mb;
+          smem[plane_bytes + off] = (uint8_t)sb;
+          tpart[i] = __builtin_popcount(mb) - 2 * __builtin_popcount(sb);
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 1; h < SLOTS; h <<= 1)
+      if (2 * h <= runs)
+#pragma unroll
+        for (int i = 0; i + h < SLOTS; i += 2 * h) {
+          kn[i] = kn[i] + kn[i + h];
+          cnt[i] = cnt[i] + cnt[i + h];
+          tpart[i] = tpart[i] + tpart[i + h];
+        }
+#pragma unroll
+    for (int i = 0; i < SLOTS; i += 1) {
+      if ((i & (runs - 1)) == 0 && (i >> lr) < gm) {
+        const float v = butterfly(part ? kn[i] : 0.0f);
+        int c = part ? cnt[i] : 0, tp = part ? tpart[i] : 0;
+#pragma unroll
+        for (int b = 0; b < 6; ++b)
+          if ((1 << b) < lanes) {
+            c += __shfl_xor(c, 1 << b, kWave);
+            tp += __shfl_xor(tp, 1 << b, kWave);
+          }
+        if (lane == 0 && wid < nw) {
+          red2[(i >> lr) * 8 + wid] = v;
+          ired[(i >> lr) * 8 + wid] = c;
+          if (tp) atomicAdd(&tw[m0 + (i >> lr)], tp);  // one add per wave and row
+        }
+      }
+    }
+    barrier();
+    if (out_planes) {
+      // The group's rows of the staged planes (its chunk range, zero padding
+      // included) to global memory, 16 or 8 bytes at a time.
+      const int units = chunks * 4 * gm;
+      for (int u = t; u < units; u += blockDim.x) {
+        const int gi = u % gm, q = u / gm, cl = q >> 2, gg = q & 3;
+        const int64_t byte = (int64_t)(kc0 + cl) * 64 + gg * 16;
+        if (byte >= row_bytes) continue;
+        const uint32_t off = (uint32_t)(((cl * 4 + gg) * M + m0 + gi) * 16);
+        const int64_t dst = (int64_t)(m0 + gi) * row_bytes + byte;
+        const uint64_t* ms = reinterpret_cast<const uint64_t*>(smem + off);
+        const uint64_t* ss = reinterpret_cast<const uint64_t*>(smem + plane_bytes + off);
+        *reinterpret_cast<uint64_t*>(o_mask + dst) = ms[0];
+        *reinterpret_cast<uint64_t*>(o_sign + dst) = ss[0];
+        if (byte + 8 < row_bytes) {
+          *reinterpret_cast<uint64_t*>(o_mask + dst + 8) = ms[1];
+          *reinterpret_cast<uint64_t*>(o_sign + dst + 8) = ss[1];
+        }
+      }
+    }
+    if (t < gm) {
+      const float ktot = tree16(red2 + t * 8, nw);
+      int ctot = 0;
+      for (int q = 0; q < nw; ++q) ctot += ired[t * 8 + q];
+      const float alpha = ctot ? ktot / (float)ctot : 0.0f;
+      s_alpha[m0 + t] = alpha;
+      s_nnz[m0 + t] = ctot;
+      if (out_scales) {
+        o_alpha[m0 + t] = alpha;
+        o_nnz[m0 + t] = ctot;
+      }
+    }
+  }
+}
+
 // RES: two-plane residual weights (planes interleaved in groups of 32 rows), N
 // counts outputs.  The wave of output tile o (16 outputs) streams both of its
 // plane tiles - rows 64 (o / 2) + 16 (o % 2) and 32 rows further - with half as
@@ -145,19 +585,36 @@ __host__ __device__ inline LdsLayout lds_layout(bool expanded, int chunks, int M
 //
 // XB: K split across blocks (a workspace is given).  blockIdx.y = ky picks the
 // block's contiguous chunk range, one of gridDim.y; the block stages only that
-// range, every wave (S = 1) multiplies its tile over it and stores the exact
-// int32 partial T_ky - 2 U_ky of its 16 x 16 outputs to the workspace, then
+// range, every wave (S = 1) multiplies its tile over it, stores the exact int32
+// partial T_ky - 2 U_ky of its 16 x 16 outputs in its slot of the workspace and
 // counts itself in the tile's arrival counter.  The last of the gridDim.y blocks
 // to arrive adds the partials (integers: the order does not matter), applies the
 // epilogue and returns the counter to zero, so no block ever waits for another.
-template <int S, bool X, int OUT, bool RES = false, bool XB = false>
+//
+// XT: the activations arrive as fp32 (1) or bf16 (2) rows in io.X and the block
+// ternarizes them itself (fused_ternarize) into the raw staging layout; a_mask,
+// a_sign and a_alpha are not read.
+struct FusedIO {
+  const void* X;
+  int64_t ldx;
+  int K;             // logical row length
+  uint8_t* o_mask;   // optional outputs (NULL: not written)
+  uint8_t* o_sign;
+  float* o_alpha;
+  int32_t* o_nnz;
+};
+
+template <int S, bool X, int OUT, bool RES = false, bool XB = false, int XT = 0>
 __global__ void __launch_bounds__(kMaxW * kWave)
 gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__ a_sign,
                  const float* __restrict__ a_alpha, int M, const uint8_t* __restrict__ w_sign,
                  const float* __restrict__ w_alpha, int64_t N, int row_bytes,
                  void* __restrict__ Y, int64_t ldy, int* __restrict__ ws_ctr,
-                 int* __restrict__ ws_part) {
+                 int* __restrict__ ws_part, FusedIO io) {
   static_assert(!XB || (S == 1 && !RES), "the cross-block split runs unsplit one-plane waves");
+  static_assert(XT == 0 || (!X && !RES), "fused ternarization stages raw one-plane operands");
+  __shared__ float s_alpha[16], s_red[16 * 8], s_red2[16 * 8];
+  __shared__ int s_nnz[16], s_ired[16 * 8];
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int W = blockDim.x / kWave;
   const int R = W / S;  // row groups per block
@@ -206,9 +663,11 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     if constexpr (RES)
       ab2 = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
                                         ars, (int)(n < N ? (uint32_t)((pn + 32) * 4) : kOOB), 0, 0));
-    const __amdgpu_buffer_rsrc_t aars = checked_rsrc(a_alpha, (uint32_t)M * 4u);
-    aa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                       aars, (int)((l_item & 15) * 4), 0, 0));
+    if constexpr (XT == 0) {
+      const __amdgpu_buffer_rsrc_t aars = checked_rsrc(a_alpha, (uint32_t)M * 4u);
+      aa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         aars, (int)((l_item & 15) * 4), 0, 0));
+    }
   }
   // 2. Staging loads, 16 bytes per plane and unit u = (m * chunks + c) * 4 + g
   //    over the M live rows (row-major, so one load instruction reads whole
@@ -228,7 +687,7 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     m = fdiv(q, chunks, inv_c);
     c = q - m * chunks;
   };
-  const int nsu = (units + (int)blockDim.x - 1) / (int)blockDim.x;  // rounds, uniform
+  const int nsu = XT ? 0 : (units + (int)blockDim.x - 1) / (int)blockDim.x;  // rounds, uniform
   const __amdgpu_buffer_rsrc_t mrs = checked_rsrc(a_mask, (uint32_t)M * (uint32_t)row_bytes);
   const __amdgpu_buffer_rsrc_t srs = checked_rsrc(a_sign, (uint32_t)M * (uint32_t)row_bytes);
   v4u sm[kMaxSU], ss[kMaxSU];
@@ -276,6 +735,22 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   //    m >= M read a cleared extra chunk.
   int* tw = tsum + wid * 16;
   if (lane < 16) tw[lane] = 0;
+  if constexpr (XT != 0) {
+    // Clear the raw planes (bytes no run covers must read 0), then ternarize.
+    for (uint32_t z = threadIdx.x * 16u; z < L.zero_off + 32u; z += blockDim.x * 16u)
+      *reinterpret_cast<v4u*>(smem + z) = v4u{0u, 0u, 0u, 0u};
+    const bool first = blockIdx.x == 0;
+    if constexpr (XT == 1)
+      fused_ternarize<float>(static_cast<const float*>(io.X), io.ldx, M, io.K,
+                             row_bytes, kc0, chunks, smem, L.plane, tw, s_alpha, s_nnz, s_red,
+                             s_red2, s_ired, io.o_mask, io.o_sign, io.o_alpha, io.o_nnz,
+                             first && io.o_mask, first && ky == 0 && io.o_alpha);
+    else
+      fused_ternarize<uint16_t>(static_cast<const uint16_t*>(io.X), io.ldx, M, io.K,
+                                row_bytes, kc0, chunks, smem, L.plane, tw, s_alpha, s_nnz, s_red,
+                                s_red2, s_ired, io.o_mask, io.o_sign, io.o_alpha, io.o_nnz,
+                                first && io.o_mask, first && ky == 0 && io.o_alpha);
+  }
   auto stage_unit = [&](int u, v4u vm, v4u vs) {
     int m, c, gg;
     unit_pos(u, m, c, gg);
@@ -316,7 +791,8 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     const int u = (int)threadIdx.x + k * (int)blockDim.x;
     if (k < nsu && u < units) stage_unit(u, sm[k], ss[k]);
   }
-  for (int u = (int)threadIdx.x + kMaxSU * (int)blockDim.x; u < units; u += (int)blockDim.x) {
+  for (int u = (int)threadIdx.x + kMaxSU * (int)blockDim.x; XT == 0 && u < units;
+       u += (int)blockDim.x) {
     int m, c, gg;
     unit_pos(u, m, c, gg);
     const uint32_t off = (uint32_t)(m * row_bytes + 64 * (kc0 + c) + 16 * gg);
@@ -326,7 +802,7 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   if constexpr (X) {
     for (int z = threadIdx.x; z < 256; z += blockDim.x)  // the extra chunk
       *reinterpret_cast<v4u*>(smem + (uint32_t)chunks * 4096u + z * 16) = v4u{0u, 0u, 0u, 0u};
-  } else {
+  } else if constexpr (XT == 0) {
     if (threadIdx.x < 2)
       *reinterpret_cast<v4u*>(smem + L.zero_off + 16 * threadIdx.x) = v4u{0u, 0u, 0u, 0u};
   }
@@ -334,6 +810,7 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   for (int b = 1; b < kNB; ++b) issue(b, c0 + b * PF);
   __builtin_amdgcn_sched_barrier(0);
   lds_barrier();
+  if constexpr (XT != 0) aa = s_alpha[l_item & 15];  // 0 for rows m >= M (never stored)
 
   // 5. Main loop.  Raw B operand of lane (r, g) for chunk c: slot (c, g, r) when
   //    r < M, else the zeroed slot (mask 0 makes every product 0).
@@ -461,23 +938,37 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
       v4i part;
 #pragma unroll
       for (int u = 0; u < 4; ++u) part[u] = tm - 2 * (int)acc[u];  // exact integers
+      // The partial goes to this split's slot of the tile with device-coherent
+      // stores (agent-scope atomic stores: sc1, visible to every XCD once
+      // complete, with no write-back or invalidation of the XCD's L2 as a fence
+      // would do); after they have completed (the wait) the block counts itself
+      // in, and the last block reads the other slots with device-coherent loads.
       const int64_t tiles_all = (N + 15) / 16;
-      *reinterpret_cast<v4i*>(ws_part + ((ky * tiles_all + ot) * kWave + lane) * 4) = part;
-      // Release this wave's partial device-wide, then count the block in.
-      __threadfence();
+      auto slot = [&](int k2) {
+        return reinterpret_cast<uint64_t*>(ws_part + ((k2 * tiles_all + ot) * kWave + lane) * 4);
+      };
+      uint64_t* mine = slot(ky);
+      __hip_atomic_store(mine, (uint64_t)(uint32_t)part[0] | ((uint64_t)(uint32_t)part[1] << 32),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(mine + 1, (uint64_t)(uint32_t)part[2] | ((uint64_t)(uint32_t)part[3] << 32),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(vmcnt_wait0());
       int old = 0;
-      if (lane == 0) old = atomicAdd(ws_ctr + ot, 1);
+      if (lane == 0)
+        old = __hip_atomic_fetch_add(ws_ctr + ot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       old = __shfl(old, 0, kWave);
-      if (old == nsplit - 1) {  // every other split has stored its partial
-        __threadfence();  // acquire: their partials are visible from here on
-        v4i sum = v4i{0, 0, 0, 0};
+      if (old == nsplit - 1) {  // every other split's slot is complete
+        v4i sum = part;
         for (int k2 = 0; k2 < nsplit; ++k2) {
-          const v4i o2 = k2 == ky ? part
-                                  : *reinterpret_cast<const v4i*>(
-                                        ws_part + ((k2 * tiles_all + ot) * kWave + lane) * 4);
-          sum += o2;
+          if (k2 == ky) continue;
+          const uint64_t* o2 = slot(k2);
+          const uint64_t lo = __hip_atomic_load(o2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t hi = __hip_atomic_load(o2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          sum += v4i{(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi,
+                     (int)(uint32_t)(hi >> 32)};
         }
-        if (lane == 0) ws_ctr[ot] = 0;  // the counter is zero again for the next call
+        if (lane == 0)  // the counter is zero again for the next call
+          __hip_atomic_store(ws_ctr + ot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         v4f a1;
 #pragma unroll
         for (int u = 0; u < 4; ++u) a1[u] = (float)sum[u];  // |acc| <= K < 2^24: exact
@@ -540,10 +1031,10 @@ Geometry geometry(int64_t N, int64_t row_bytes, int64_t mg, int accs = 1) {
 // staging only its range (LLaMA2-70B down, K = 28672: 28 KiB of planes per block
 // at M = 16 instead of 112 KiB, and expanded B operands instead of raw words).
 // The workspace starts with a fixed region of kCtrBytes for the arrival
-// counters (one per tile, zero between calls), followed by P int32 partial
-// tiles of 16 x 16 per tile.  The counter region is the same for every shape:
-// partials never reach into it, so the counters of any later call, whatever its
-// tile count, start at zero.
+// counters (one per tile, zero between calls: the last block of a tile clears
+// its counter), followed by P int32 partial tiles of 16 x 16 per output tile.
+// The counter region is the same for every shape, so a later call, whatever its
+// tile count, finds its counters zero (partials never reach into it).
 struct Split {
   bool use = false;
   int P = 1, R = 1;
@@ -557,7 +1048,10 @@ constexpr size_t kCtrBytes = 8192;        // counters of up to 2048 tiles (P >= 
 
 Split split_plan(int64_t M, int64_t N, int64_t row_bytes) {
   Split sp;
-  if (M < 1 || M > 16 || N >= ((int64_t)1 << 29)) return sp;
+  // From 8 activation rows on: there the staged planes are a large share of a
+  // block's bytes (70B down at M = 16: 10.8 us split against 14.4 us); at M = 4
+  // the partials' round trip costs more than it saves (10.5 against 9.1 us).
+  if (M < 8 || M > 16 || N >= ((int64_t)1 << 29)) return sp;
   const Geometry q1 = geometry(N, row_bytes, M);
   const int64_t tiles = (N + 15) / 16;
   const int64_t chunks = (row_bytes + 63) / 64;
@@ -580,21 +1074,80 @@ Split split_plan(int64_t M, int64_t N, int64_t row_bytes) {
   return sp;
 }
 
-template <int S, bool X, int OUT, bool RES = false, bool XB = false>
+// io: the fused ternarization's rows (XT != 0; offset here to the group's rows).
+template <int S, bool X, int OUT, bool RES = false, bool XB = false, int XT = 0>
 hipError_t launch_s(const GemmArgs& g, const Geometry& q, int64_t m0, int64_t mg,
                     int64_t row_bytes, hipStream_t stream, int splits = 1, int* ctr = nullptr,
-                    int* part = nullptr) {
-  auto kfn = gemv_mfma_kernel<S, X, OUT, RES, XB>;
+                    int* part = nullptr, FusedIO io = FusedIO{}) {
+  auto kfn = gemv_mfma_kernel<S, X, OUT, RES, XB, XT>;
   hipError_t e = hipFuncSetAttribute((const void*)kfn,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)q.lds);
   if (e != hipSuccess) return e;
   constexpr int ES = OUT == (int)Elt::BF16 ? 2 : 4;
+  if constexpr (XT != 0) {
+    io.X = static_cast<const char*>(io.X) + m0 * io.ldx * (XT == 1 ? 4 : 2);
+    if (io.o_mask) io.o_mask += m0 * row_bytes;
+    if (io.o_sign) io.o_sign += m0 * row_bytes;
+    if (io.o_alpha) io.o_alpha += m0;
+    if (io.o_nnz) io.o_nnz += m0;
+  }
+  const uint8_t* am = g.a_mask ? g.a_mask + m0 * row_bytes : nullptr;
+  const uint8_t* as = g.a_sign ? g.a_sign + m0 * row_bytes : nullptr;
   hipLaunchKernelGGL(kfn, dim3((unsigned)q.blocks, (unsigned)splits),
-                     dim3((unsigned)(q.S * q.R * kWave)), q.lds, stream,
-                     g.a_mask + m0 * row_bytes, g.a_sign + m0 * row_bytes,
+                     dim3((unsigned)(q.S * q.R * kWave)), q.lds, stream, am, as,
                      g.a_alpha ? g.a_alpha + m0 : nullptr, (int)mg, g.b_sign, g.b_alpha, g.N,
-                     (int)row_bytes, static_cast<char*>(g.Y) + m0 * g.ldy * ES, g.ldy, ctr, part);
+                     (int)row_bytes, static_cast<char*>(g.Y) + m0 * g.ldy * ES, g.ldy, ctr, part,
+                     io);
   return hipGetLastError();
+}
+
+// Fused decode (XT = 1 fp32, 2 bf16 activations): raw staging only; the same
+// cross-block split as launch_out when a workspace is given, else groups of
+// activation rows whose raw planes fit in LDS.
+template <int OUT, int XT>
+hipError_t launch_fused(const GemmArgs& g, const FusedIO& io, hipStream_t stream) {
+  if (g.N >= (int64_t)1 << 29) return hipErrorInvalidValue;  // 32-bit offsets
+  const int64_t row_bytes = (g.K + 63) / 64 * 8;
+  const Split sp = g.ws ? split_plan(g.M, g.N, row_bytes) : Split{};
+  if (sp.use) {
+    if (g.ws_bytes < sp.ws_bytes) return hipErrorInvalidValue;  // checked by the caller
+    const int64_t chunks = (row_bytes + 63) / 64;
+    const int64_t cb = (chunks + sp.P - 1) / sp.P;
+    Geometry q;
+    q.S = 1;
+    q.R = sp.R;
+    q.X = false;
+    q.blocks = sp.blocks;
+    q.lds = lds_layout(false, (int)cb, (int)g.M, 1, sp.R).total;
+    if (q.lds > kMaxLds) return hipErrorInvalidValue;
+    int* ctr = static_cast<int*>(g.ws);
+    int* part = reinterpret_cast<int*>(static_cast<char*>(g.ws) + sp.ctr_bytes);
+    return launch_s<1, false, OUT, false, true, XT>(g, q, 0, g.M, row_bytes, stream, sp.P, ctr,
+                                                    part, io);
+  }
+  auto raw = [&](int64_t mg) {
+    Geometry q = geometry(g.N, row_bytes, mg);
+    q.X = false;
+    q.lds = lds_layout(false, (int)((row_bytes + 63) / 64), (int)mg, q.S, q.R).total;
+    q.fits = q.lds <= kMaxLds;
+    return q;
+  };
+  int64_t mg = g.M;
+  while (mg > 1 && !raw(mg).fits) mg = (mg + 1) / 2;
+  for (int64_t m0 = 0; m0 < g.M; m0 += mg) {
+    const int64_t cnt = g.M - m0 < mg ? g.M - m0 : mg;
+    const Geometry q = raw(cnt);
+    if (!q.fits) return hipErrorInvalidValue;
+    hipError_t e;
+    switch (q.S) {
+      case 1: e = launch_s<1, false, OUT, false, false, XT>(g, q, m0, cnt, row_bytes, stream, 1, nullptr, nullptr, io); break;
+      case 2: e = launch_s<2, false, OUT, false, false, XT>(g, q, m0, cnt, row_bytes, stream, 1, nullptr, nullptr, io); break;
+      case 4: e = launch_s<4, false, OUT, false, false, XT>(g, q, m0, cnt, row_bytes, stream, 1, nullptr, nullptr, io); break;
+      default: e = launch_s<8, false, OUT, false, false, XT>(g, q, m0, cnt, row_bytes, stream, 1, nullptr, nullptr, io); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <bool X, int OUT, bool RES = false>
@@ -722,6 +1275,22 @@ hipError_t scratch_workspace(void** ptr, hipStream_t stream) {
 size_t gemv_mfma_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   const Split sp = split_plan(M, N, (K + 63) / 64 * 8);
   return sp.use ? sp.ws_bytes : 0;
+}
+
+hipError_t launch_gemv_fused(const GemmArgs& g, const void* X, Elt x_dt, int64_t ldx,
+                             uint8_t* o_mask, uint8_t* o_sign, float* o_alpha, int32_t* o_nnz,
+                             hipStream_t stream) {
+  const FusedIO io{X, ldx, (int)g.K, o_mask, o_sign, o_alpha, o_nnz};
+  const bool bf = x_dt == Elt::BF16;
+  switch (g.y_dt) {
+    case Elt::F32:
+      return bf ? launch_fused<(int)Elt::F32, 2>(g, io, stream) : launch_fused<(int)Elt::F32, 1>(g, io, stream);
+    case Elt::BF16:
+      return bf ? launch_fused<(int)Elt::BF16, 2>(g, io, stream) : launch_fused<(int)Elt::BF16, 1>(g, io, stream);
+    case Elt::I32:
+      return bf ? launch_fused<(int)Elt::I32, 2>(g, io, stream) : launch_fused<(int)Elt::I32, 1>(g, io, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv_mfma(const GemmArgs& g, hipStream_t stream) {

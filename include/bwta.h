@@ -143,10 +143,10 @@ bwta_status bwta_ternarize_pack(const void* X, bwta_dtype x_dtype, int64_t rows,
                                 int32_t* nnz, void* stream);
 
 /* Workspace (bwta_gemm, bwta_gemv).  A product may split its K range across
- * thread blocks; each block then writes an exact int32 partial of its outputs
- * to the workspace and counts itself in a per-tile arrival counter there, and
- * the last block of a tile adds the partials, applies the epilogue and sets the
- * counter back to zero.  The decode kernel does so where it would otherwise
+ * thread blocks; each block then stores an exact int32 partial of its outputs
+ * in the workspace (device-coherent stores) and counts itself in a per-tile
+ * arrival counter there, and the last block of a tile adds the partials,
+ * applies the epilogue and sets the counter back to zero.  The decode kernel does so where it would otherwise
  * split K inside a block (fewer than 1536 tiles of 16 weight rows, LLaMA2-70B
  * down for example).
  *   workspace = NULL: no cross-block split (ws_bytes is ignored); the result is
@@ -209,6 +209,28 @@ bwta_status bwta_gemv(const uint8_t* a_mask, const uint8_t* a_sign, const float*
                       const int32_t* a_nnz, const uint8_t* w_sign, const float* w_alpha,
                       int64_t M, int64_t N, int64_t K, void* Y, bwta_dtype y_dtype, int64_t ldy,
                       bwta_algo algo, void* workspace, size_t ws_bytes, void* stream);
+
+/* Decode linear in one launch (page: Abstract, ternary activations projected
+ * online and a bit-packed binary/ternary MatMul; the replies quoted on the page
+ * name decode as a workload): ternarize the M rows of X by the rule of
+ * bwta_ternarize_pack and multiply them with the binary weights as bwta_gemv
+ * does, without the activation planes going through memory.  Every thread
+ * block ternarizes the rows itself (M * K values per block), so the call pays
+ * off where the weights dominate: decode rows against large weight matrices.
+ * X: M x K, row m at X + m * ldx elements, unit stride along k, BWTA_F32 or
+ *    BWTA_BF16; 0 <= M <= 16 (else BWTA_ERR_UNSUPPORTED).
+ * w_sign, w_alpha, Y, y_dtype, ldy: as for bwta_gemv (the FP4 decode kernel).
+ * a_mask, a_sign (M * row_bytes(K) bytes each, 16-byte aligned) and a_alpha,
+ *    a_nnz (M entries): optional outputs, the ternarized planes and scales as
+ *    bwta_ternarize_pack would write them; NULL (each pair together) = not
+ *    written.
+ * workspace, ws_bytes: as for bwta_gemv, sized by
+ *    bwta_gemv_workspace_size(M, N, K, BWTA_ALGO_MFMA). */
+bwta_status bwta_gemv_fused(const void* X, bwta_dtype x_dtype, int64_t ldx, const uint8_t* w_sign,
+                            const float* w_alpha, int64_t M, int64_t N, int64_t K, void* Y,
+                            bwta_dtype y_dtype, int64_t ldy, uint8_t* a_mask, uint8_t* a_sign,
+                            float* a_alpha, int32_t* a_nnz, void* workspace, size_t ws_bytes,
+                            void* stream);
 
 /* bwta_gemv for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same

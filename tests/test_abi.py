@@ -95,7 +95,7 @@ def test_gemv_rejects_m_above_16(L):
 
 def test_workspace_size_query(L):
     """The decode kernel splits K across blocks where it would otherwise split it
-    inside a block: LLaMA2-70B down (N = 8192, K = 28672) from two rows on, not
+    inside a block: LLaMA2-70B down (N = 8192, K = 28672) from 8 rows on, not
     gate/up (1792 tiles of 16 rows) and not the M = 1 popcount kernel."""
     gv, gm = L.bwta_gemv_workspace_size, L.bwta_gemm_workspace_size
     AUTO, MFMA, POPC = 0, 1, 2
@@ -103,10 +103,11 @@ def test_workspace_size_query(L):
     assert need > 0 and need % 256 == 0
     assert need >= 512 * 16 * 16 * 4 * 2          # at least two int32 partial tiles each
     assert need <= (4 << 20) + (8 << 10)          # the stated cap on partials
-    assert gv(4, 8192, 28672, AUTO) == need       # one tile of 16 rows holds M <= 16
+    assert gv(8, 8192, 28672, AUTO) == need       # one tile of 16 rows holds M <= 16
+    assert gv(4, 8192, 28672, AUTO) == 0          # below 8 rows the split does not pay
     assert gv(16, 8192, 28672, MFMA) == need
     assert gv(1, 8192, 28672, AUTO) == 0          # popcount GEMV
-    assert gv(1, 8192, 28672, MFMA) > 0           # M = 1 on the FP4 decode kernel
+    assert gv(1, 8192, 28672, MFMA) == 0
     assert gv(16, 8192, 28672, POPC) == 0
     assert gv(16, 28672, 8192, AUTO) == 0         # enough tiles: no split
     assert gv(17, 8192, 28672, AUTO) == 0 and gv(0, 8192, 28672, AUTO) == 0

@@ -1,0 +1,78 @@
+"""GPU parity of bwta_gemv_fused (decode linear with the ternarization fused into
+the decode kernel) against the oracle.
+
+The kernel's own ternarization (returned planes, alpha, nnz) must equal the
+oracle's ternarize() of the same rows bit for bit, and so must the int32
+accumulators, fp32 outputs and bf16 outputs computed from it.  Shapes cover
+the vector load path (K a multiple of 8, aligned rows) and the element path
+(ragged K, or a row stride that breaks 16-byte alignment), trees over fewer
+lanes than a block (small K), the block-internal K split and the cross-block
+split (with a workspace), and rows with zeros, signed zeros and outliers."""
+import numpy as np
+import pytest
+
+from tests.helpers import to_dev, to_host
+from tests.test_parity_gpu import _w, _x
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1, 1000, 1024), (2, 513, 8192), (4, 300, 28672), (16, 300, 28672), (3, 77, 200),
+          (1, 40, 65536), (5, 100, 100), (7, 257, 1000), (4, 33, 64), (1, 17, 1),
+          (16, 1000, 28736), (9, 600, 36928)]
+
+
+@pytest.fixture(scope="module")
+def bw():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import binary_ternary_matmul_amd as b
+    b.lib()
+    return b
+
+
+def _check(bw, oracle, x, w, Xd, ws):
+    wp = bw.bwta_pack_weights(to_dev(w))
+    t, alpha, nnz = oracle.ternarize(x)
+    s, w_alpha = oracle.binarize(w)
+    acc_ref = oracle.matmul_i32(t, s, threads=8)
+    acc, tp = bw.bwta_gemv_fused(Xd, wp, "i32", planes=True, workspace=ws)
+    assert (to_host(tp.mask) == oracle.pack_plane(t, "mask")).all(), "mask plane differs"
+    assert (to_host(tp.sign) == oracle.pack_plane(t, "sign")).all(), "sign plane differs"
+    assert (to_host(tp.alpha).view(np.uint32) == alpha.view(np.uint32)).all(), "alpha differs"
+    assert (to_host(tp.nnz) == nnz).all(), "nnz differs"
+    assert (to_host(acc) == acc_ref).all(), "accumulators differ"
+    y_ref = oracle.scale(acc_ref, alpha, w_alpha)
+    y = to_host(bw.bwta_gemv_fused(Xd, wp, "f32", workspace=ws))
+    assert (y.view(np.uint32) == y_ref.view(np.uint32)).all(), "fp32 outputs differ"
+    yb = to_host(bw.bwta_gemv_fused(Xd, wp, "bf16", workspace=ws))
+    assert (yb == oracle.to_bf16(y_ref)).all(), "bf16 outputs differ"
+
+
+@pytest.mark.parametrize("ws", [None, "auto"])
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemv_fused(bw, oracle, M, N, K, bf16, ws):
+    x = _x(M * 31 + N + K, M, K, bf16)
+    w = _w(N + K, N, K)
+    _check(bw, oracle, x, w, to_dev(x), ws)
+
+
+@pytest.mark.parametrize("pad", [8, 3])
+def test_gemv_fused_row_stride(bw, oracle, pad):
+    """Rows taken from a wider tensor (ldx = K + pad): pad 8 keeps bf16 rows
+    16-byte aligned, pad 3 does not (element loads)."""
+    M, N, K = 6, 700, 4096
+    xw = _x(77 + pad, M, K + pad, True)
+    x = np.ascontiguousarray(xw[:, :K])
+    w = _w(5, N, K)
+    _check(bw, oracle, x, w, to_dev(xw)[:, :K], "auto")
+
+
+def test_gemv_fused_zero_rows(bw, oracle):
+    """All-zero rows (nnz 0, alpha 0, outputs 0) next to normal ones."""
+    M, N, K = 4, 300, 28672
+    x = _x(9, M, K, True)
+    x[1] = 0
+    x[3] = 0x8000  # -0.0 in every column
+    _check(bw, oracle, x, _w(10, N, K), to_dev(x), "auto")

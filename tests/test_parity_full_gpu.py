@@ -149,6 +149,32 @@ def test_full_llama70b_decode(bw, oracle, shape):
         assert (y.view(np.uint32) == ref_y.view(np.uint32)).all(), f"M={M}: outputs differ"
 
 
+
+@pytest.mark.parametrize("shape", [n for n, _, _ in inputs.LLAMA70B_DECODE_SHAPES])
+def test_full_llama70b_decode_fused(bw, oracle, shape):
+    """The decode linear in one launch (bwta_gemv_fused: ternarize inside the
+    decode kernel) on the full 70B-shaped weights, M = 1, 4, 16, bf16 in, fp32
+    out, with the shared workspace: the kernel's planes, alpha and nnz, every
+    accumulator and every output."""
+    lins = {M: [l for l in inputs.llama70b_decode(M) if l.name == shape][0] for M in (1, 4, 16)}
+    w = lins[16].w()
+    wp = bw.bwta_pack_weights(to_dev(w))
+    s, w_alpha = _check_weights(bw, oracle, wp, w)
+    del w
+    for M, lin in lins.items():
+        x = lin.x()
+        t, a_alpha, nnz = oracle.ternarize(x)
+        acc, tp = bw.bwta_gemv_fused(to_dev(x), wp, "i32", planes=True)
+        assert (to_host(tp.mask) == oracle.pack_plane(t, "mask")).all(), f"M={M}: mask"
+        assert (to_host(tp.sign) == oracle.pack_plane(t, "sign")).all(), f"M={M}: sign"
+        assert (to_host(tp.alpha).view(np.uint32) == a_alpha.view(np.uint32)).all()
+        assert (to_host(tp.nnz) == nnz).all()
+        ref_acc = oracle.matmul_i32(t, s, threads=THREADS)
+        assert (to_host(acc) == ref_acc).all(), f"M={M}: accumulators differ"
+        y = to_host(bw.bwta_gemv_fused(to_dev(x), wp, "f32"))
+        ref_y = oracle.scale(ref_acc, a_alpha, w_alpha)
+        assert (y.view(np.uint32) == ref_y.view(np.uint32)).all(), f"M={M}: outputs differ"
+
 def test_full_llama70b_gate_up_stacked(bw, oracle):
     """Gate and up of one 70B MLP stacked into one [57344, 8192] weight (one decode
     launch for both), M = 1, 4, 16, algo auto, fp32 out: every output."""

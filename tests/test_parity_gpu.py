@@ -274,7 +274,7 @@ def test_gemv_workspace_reuse(bw, oracle):
     (a later call with more tiles must not find an earlier call's partials where
     its counters are)."""
     import torch
-    cases = [(16, 1000, 28736), (16, 1000, 28736), (3, 300, 9000), (7, 513, 16384),
+    cases = [(16, 1000, 28736), (16, 1000, 28736), (9, 300, 9000), (8, 513, 16384),
              (16, 4100, 17000)]   # more tiles than any call before it
     need = max(bw.bwta_gemv_workspace_size(M, N, K) for M, N, K in cases)
     assert need > 0

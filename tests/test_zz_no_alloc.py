@@ -52,7 +52,7 @@ def _noalloc(bw, a, wp, out, out_dtype):
 
 def test_gemv_noalloc_matches_gemv(bw, oracle):
     import torch
-    cases = [(16, 8192, 28672, 11), (4, 3000, 17000, 12), (16, 8192, 28672, 13)]
+    cases = [(16, 8192, 28672, 11), (8, 3000, 17000, 12), (16, 8192, 28672, 13)]
     for i, (M, N, K, seed) in enumerate(cases):
         need = bw.bwta_gemv_workspace_size(M, N, K)
         assert need > 0, "the case must run the split that uses the scratch array"
