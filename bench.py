@@ -123,6 +123,45 @@ def profiled_traffic(key):
     return None
 
 
+def ceilings(copies=24):
+    """The chip's measured ceilings (libbwta_probe.so): read-only HBM streams of
+    one decode weight's size (29.59 MB, each launch reading another of `copies`
+    buffers so that it comes from HBM) and of 1 GiB, and matrix-core loops of
+    16 independent FP4 (e2m1) and int8 products per wave on all 1024 SIMDs."""
+    import ctypes
+    import torch
+    from binary_ternary_matmul_amd import build
+    P = ctypes.CDLL(build.PROBE_LIB)
+    V = ctypes.c_void_p
+    P.bwta_probe_stream_read.argtypes = [V, ctypes.c_size_t, V, ctypes.c_int, V]
+    P.bwta_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, V, V]
+    st = lambda: V(torch.cuda.current_stream().cuda_stream)
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    out = {}
+    nb = 29591552                                      # 70B gate/up decode bytes, rounded to 16
+    bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    for b in bufs:
+        b.fill_(1)
+
+    def small():
+        for b in bufs:
+            assert P.bwta_probe_stream_read(V(b.data_ptr()), nb, V(sink.data_ptr()), 0, st()) == 0
+    ms = time_calls(small, reps=2) / copies
+    out["hbm_read_29.6MB_GBps"] = round(nb / (ms * 1e-3) / 1e9, 1)
+    del bufs
+    big = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    ms = time_calls(lambda: P.bwta_probe_stream_read(V(big.data_ptr()), big.numel(),
+                                                       V(sink.data_ptr()), 0, st()), reps=3)
+    out["hbm_read_1GiB_GBps"] = round(big.numel() / (ms * 1e-3) / 1e9, 1)
+    del big
+    for fmt, name, per in ((0, "fp4_mfma_loop_TOPS", 131072), (1, "int8_mfma_loop_TOPS", 65536)):
+        iters = 1500
+        ms = time_calls(lambda fmt=fmt: P.bwta_probe_mfma(fmt, 1024, iters, V(sink.data_ptr()),
+                                                          st()), reps=3)
+        out[name] = round(1024 * iters * 16 * per / (ms * 1e-3) / 1e12, 1)
+    return out
+
+
 def bench_prefill(bw, steps, warmup, M=2048):
     import torch
     from binary_ternary_matmul_amd import inputs
@@ -315,13 +354,37 @@ def bench_gemv(bw, copies=24, reps=4):
                                       "bytes": int(nbytes), "GBps": round(gbs, 1),
                                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
                                       "traffic": tr["bytes"] if tr else None}
+    # The decode linear end to end (one step of a decoder: bf16 activations in),
+    # per shape and M: ternarize + bwta_gemv as two launches, and bwta_gemv_fused
+    # (one launch that ternarizes inside the decode kernel).
+    e2e = {}
+    for M in (1, 4, 16):
+        for lin in inputs.llama70b_decode(M):
+            ws = out["_w"][lin.name]
+            X = dev(lin.x())
+            y = torch.empty((M, lin.N), dtype=torch.float32, device="cuda")
+
+            def two(X=X, y=y, ws=ws):
+                for wi in ws:
+                    bw.bwta_gemv(bw.bwta_ternarize_pack(X), wi, "f32", "auto", y)
+
+            def fused(X=X, y=y, ws=ws):
+                for wi in ws:
+                    bw.bwta_gemv_fused(X, wi, "f32", y)
+            u2 = time_calls(two, reps=reps) * 1e3 / len(ws)
+            uf = time_calls(fused, reps=reps) * 1e3 / len(ws)
+            e2e[f"{lin.name}_M{M}"] = {"ternarize_plus_gemv_us": round(u2, 2),
+                                       "fused_us": round(uf, 2),
+                                       "faster": "fused" if uf < u2 else "two_launches"}
+    out["decode_linear_end_to_end"] = e2e
     out.pop("_w", None)
-    # The decode kernel's roofline on the gate/up shape at M = 4 (FP4 GEMV):
-    # algorithmic bytes per launch over the measured per-launch time.
-    ref = out.get("gate_up_M4")
+    # The decode kernel's roofline on the gate/up shape at M = 1 (the popcount
+    # GEMV that AUTO runs there): algorithmic bytes per launch over the measured
+    # per-launch time.
+    ref = out.get("gate_up_M1")
     if ref:
-        tr = profiled_traffic("gemv_mfma_kernel.gate_up.M4")
-        out["roofline"] = {"bound": "hbm", "kernel": "gemv_mfma_kernel", "shape": "gate_up_M4",
+        tr = profiled_traffic("gemv_popcount_kernel.gate_up.M1")
+        out["roofline"] = {"bound": "hbm", "kernel": ref["kernel"], "shape": "gate_up_M1",
                            "achieved": ref["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": ref["hbm_frac"], "traffic": tr["bytes"] if tr else None}
     return out
@@ -374,8 +437,18 @@ def bench_attention(bw, reps=5, H=32, L=2048, D=128):
     ms_f = time_calls(fused, reps=reps)
     ms_fa = time_calls(fused_all, reps=reps)
     ops = 2.0 * H * L * L * D
+    rb = bw.row_bytes(D)
+    qk_bytes = 2 * (H * L * D * 2) + 2 * 2 * (2 * H * L * rb + 8 * H * L) + H * L * L * 4
     return {"heads": H, "L": L, "d": D,
             "qk_ms": round(ms_qk, 3), "qk_scores_GBps": round(H * L * L * 4 / (ms_qk * 1e-3) / 1e9, 1),
+            # Q K^T with ternarizing Q and K: bound by HBM, its algorithmic bytes are
+            # the bf16 Q and K read, their planes and scales written and read back,
+            # and the int32 scores written.
+            "qk_roofline": {"bound": "hbm", "kernel": "gemm_mfma_kernel (+ pack_rows_kernel)",
+                            "achieved": round(qk_bytes / (ms_qk * 1e-3) / 1e9, 1),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(qk_bytes / (ms_qk * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+                            "bytes": qk_bytes},
             "pv_ms": round(ms_pv, 3), "pv_tops_incl_ternarize_P": round(ops / (ms_pv * 1e-3) / 1e12, 1),
             "fused_kernel": "attention_kernel", "fused_ms": round(ms_f, 4),
             "fused_tops": round(2 * ops / (ms_f * 1e-3) / 1e12, 1),
@@ -393,10 +466,15 @@ def bench_attention(bw, reps=5, H=32, L=2048, D=128):
 
 
 def bench_bert(bw, reps=10):
+    """BERT-base encoder linears (M = 4096, fp32 in, bf16 out), each timed as
+    ternarize + product.  Roofline: these sit near the ridge, so the bound is the
+    larger of the HBM time of the algorithmic bytes (fp32 X read; activation
+    planes and scales written and read back; weight plane and scales read; bf16
+    Y written) and the FP4 matrix-core time of 2 M N K."""
     import torch
     from binary_ternary_matmul_amd import inputs
     lins = inputs.bert_encoder()
-    tot_ops, tot_ms = 0.0, 0.0
+    tot_ops, tot_ms, tot_ideal = 0.0, 0.0, 0.0
     res = {}
     for lin in lins:
         x = dev(lin.x())
@@ -405,31 +483,70 @@ def bench_bert(bw, reps=10):
         ms = time_calls(lambda x=x, w=w, y=y: bw.bwta_gemm(bw.bwta_ternarize_pack(x), w, "bf16",
                                                            "auto", y), reps=reps)
         ops = 2.0 * lin.M * lin.N * lin.K
+        rb = bw.row_bytes(lin.K)
+        nbytes = (lin.M * lin.K * 4 + 2 * (2 * lin.M * rb + 8 * lin.M) + lin.N * rb + 4 * lin.N
+                  + lin.M * lin.N * 2)
+        ideal_us = max(nbytes / (HBM_PEAK_GBS * 1e9), ops / (FP4_PEAK_TOPS * 1e12)) * 1e6
         tot_ops += ops
         tot_ms += ms
-        res[lin.name] = {"us": round(ms * 1e3, 1), "tops": round(ops / (ms * 1e-3) / 1e12, 1)}
-    return {"layer_tops_incl_ternarize": round(tot_ops / (tot_ms * 1e-3) / 1e12, 1), "per_gemm": res}
+        tot_ideal += ideal_us
+        res[lin.name] = {"us": round(ms * 1e3, 1), "tops": round(ops / (ms * 1e-3) / 1e12, 1),
+                         "bytes": int(nbytes), "roofline_us": round(ideal_us, 2),
+                         "frac": round(ideal_us / (ms * 1e3), 3)}
+    return {"layer_tops_incl_ternarize": round(tot_ops / (tot_ms * 1e-3) / 1e12, 1),
+            "roofline": {"bound": "max(hbm, mfma)", "achieved_us": round(tot_ms * 1e3, 1),
+                         "roofline_us": round(tot_ideal, 1),
+                         "frac": round(tot_ideal / (tot_ms * 1e3), 3)},
+            "per_gemm": res}
 
 
-def cpu_baseline(M=2048, rows=2048):
-    """The oracle, untouched, on the first `rows` token rows of the same step."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(M=2048, rows=2048, rows_1t=32):
+    """The oracle, untouched, on the same step: ternarize the four inputs and run
+    the seven products as a dense int32 loop, on all host threads (at most 16,
+    the cores a GPU machine gives one GPU) over all `rows` token rows, and on one
+    thread over the first `rows_1t` rows (extrapolated to `rows`).  Each step is
+    timed on its own."""
     from binary_ternary_matmul_amd import inputs
     from oracle import oracle
     acts, lins = inputs.llama7b_prefill(M)
-    xs = {name: gen()[:rows] for name, gen in acts.items()}
+    xs = {name: gen() for name, gen in acts.items()}
     ws = [(lin, oracle.binarize(lin.w())[0]) for lin in lins]   # weights are packed offline
-    threads = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    ts = {name: oracle.ternarize(x)[0] for name, x in xs.items()}
-    ops = 0.0
-    for lin, s in ws:
-        oracle.matmul_i32(ts[inputs.LLAMA7B_INPUTS[lin.name]], s, threads=threads)
-        ops += 2.0 * rows * lin.N * lin.K
-    dt = time.perf_counter() - t0
+    threads = max(1, min(16, os.cpu_count() or 1))
+
+    def leg(n, thr):
+        t0 = time.perf_counter()
+        ts = {name: oracle.ternarize(x[:n])[0] for name, x in xs.items()}
+        t1 = time.perf_counter()
+        ops = 0.0
+        for lin, s in ws:
+            oracle.matmul_i32(ts[inputs.LLAMA7B_INPUTS[lin.name]], s, threads=thr)
+            ops += 2.0 * n * lin.N * lin.K
+        t2 = time.perf_counter()
+        return t1 - t0, t2 - t1, ops
+    tern_s, gemm_s, ops = leg(rows, threads)
+    tern1, gemm1, ops1 = leg(rows_1t, 1)
+    scale = rows / rows_1t
+    dt = tern_s + gemm_s
     return {"value": round(ops / dt / 1e12, 4), "unit": "TOPS", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 2),
+            "cpu_model": _cpu_model(), "seconds": round(dt, 2),
+            "ternarize_s": round(tern_s, 3), "gemm_s": round(gemm_s, 2),
             "sample": f"ternarize + dense int32 product of the first {rows} of {M} token rows "
-                      f"of all seven LLaMA-7B layer GEMMs ({ops / 1e9:.0f} G ops)"}
+                      f"of all seven LLaMA-7B layer GEMMs ({ops / 1e9:.0f} G ops), {threads} threads",
+            "one_thread": {"rows": rows_1t, "extrapolated_to_rows": rows,
+                           "ternarize_s": round(tern1 * scale, 2),
+                           "gemm_s": round(gemm1 * scale, 1),
+                           "value": round(ops1 / (tern1 + gemm1) / 1e12, 5), "unit": "TOPS"}}
 
 
 def calibrate_copy(nbytes=256 << 20, reps=3):
@@ -489,6 +606,8 @@ def main():
                     help="only run a few cold launches of each decode GEMV shape")
     ap.add_argument("--attention", action="store_true",
                     help="only the attention section (unfused products and the fused call)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only the measured ceilings (HBM read streams, MFMA loops)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -509,6 +628,9 @@ def main():
         return
     if args.attention:
         print(json.dumps({"attention": bench_attention(bw)}), flush=True)
+        return
+    if args.ceilings:
+        print(json.dumps({"ceilings": ceilings()}), flush=True)
         return
 
     from binary_ternary_matmul_amd import inputs
@@ -548,6 +670,11 @@ def main():
         line["roofline"]["traffic_algorithmic"] = tr["algorithmic_bytes"]
         line["roofline"]["traffic_source"] = tr["summary"]
     if not args.quick:
+        log("[bench] ceilings (probe kernels)")
+        line["ceilings"] = ceilings()
+        fp4_loop = line["ceilings"]["fp4_mfma_loop_TOPS"]
+        line["roofline"]["measured_peak"] = fp4_loop
+        line["roofline"]["frac_of_measured_peak"] = round(achieved / fp4_loop, 3)
         log("[bench] int8 MFMA variant")
         line["mfma_i8"] = bench_algo(bw, pre, "mfma_i8")
         log("[bench] popcount variant")
@@ -556,6 +683,11 @@ def main():
         line["residual"] = bench_residual(bw, pre)
         log("[bench] gemv")
         line["gemv"] = bench_gemv(bw)
+        if "roofline" in line["gemv"]:
+            hb = line["ceilings"]["hbm_read_29.6MB_GBps"]
+            line["gemv"]["roofline"]["measured_peak"] = hb
+            line["gemv"]["roofline"]["frac_of_measured_peak"] = round(
+                line["gemv"]["roofline"]["achieved"] / hb, 3)
         log("[bench] gemv, two-plane residual weights")
         line["residual"]["decode"] = bench_gemv_residual(bw)
         log("[bench] attention")

@@ -1,4 +1,5 @@
-"""Build libbwta.so (HIP, gfx950) in-tree with hipcc.
+"""Build libbwta.so (HIP, gfx950) in-tree with hipcc, and libbwta_probe.so (the
+benchmark's measurement kernels, not part of the library).
 
     python -m binary_ternary_matmul_amd.build          # build if sources changed
     python -m binary_ternary_matmul_amd.build --force  # always rebuild
@@ -23,6 +24,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbwta.so")
+PROBE_LIB = os.path.join(PKG, "libbwta_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 
 SOURCES = ["pack.hip", "gemm_mfma.hip", "gemm_mfma_i8.hip", "gemm_popcount.hip", "gemv_mfma.hip",
            "attention.hip", "bwta_api.cpp"]
@@ -52,7 +55,8 @@ def _stale(target: str, deps: list[str]) -> bool:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    deps = [os.path.join(CSRC, src), os.path.join(INCLUDE, "bwta.h")] + \
+    deps = [os.path.join(CSRC, src), os.path.join(INCLUDE, "bwta.h"),
+            os.path.join(INCLUDE, "bwta_probe.h")] + \
         [os.path.join(CSRC, h) for h in HEADERS] + [__file__]
     if _stale(obj, deps):
         cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj + ".tmp"]
@@ -69,15 +73,16 @@ def build(force: bool = False, verbose: bool = False) -> str:
         for f in os.listdir(BUILD):
             if f.endswith(".o"):
                 os.remove(os.path.join(BUILD, f))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    if force or _stale(LIB, objs):
-        tmp = LIB + ".tmp%d" % os.getpid()
-        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
-        os.replace(tmp, LIB)
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    for lib, lib_objs in ((LIB, objs[:len(SOURCES)]), (PROBE_LIB, objs[len(SOURCES):])):
+        if force or _stale(lib, lib_objs):
+            tmp = lib + ".tmp%d" % os.getpid()
+            cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *lib_objs]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
+            os.replace(tmp, lib)
     if verbose:
         print(f"built {LIB}")
     return LIB

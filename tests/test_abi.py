@@ -23,8 +23,8 @@ def L():
     return _binding.lib()
 
 
-def declared_functions():
-    src = open(HEADER).read()
+def declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(bwta_[a-z_0-9]+)\s*\(", src)))
 
@@ -34,6 +34,26 @@ def test_exports_every_declared_symbol(L):
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), f"libbwta.so does not export {n}"
+
+
+def test_probe_library_exports():
+    """libbwta_probe.so (the benchmark's measurement kernels) exports what
+    include/bwta_probe.h declares and rejects bad arguments before launching."""
+    from binary_ternary_matmul_amd import build
+    if not os.path.exists(build.PROBE_LIB):
+        build.build()
+    P = ctypes.CDLL(build.PROBE_LIB)
+    names = declared_functions(os.path.join(ROOT, "include", "bwta_probe.h"))
+    assert names == ["bwta_probe_mfma", "bwta_probe_stream_read"]
+    for n in names:
+        assert hasattr(P, n)
+    V = ctypes.c_void_p
+    P.bwta_probe_stream_read.argtypes = [V, ctypes.c_size_t, V, ctypes.c_int, V]
+    P.bwta_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, V, V]
+    assert P.bwta_probe_stream_read(V(A), 100, V(A), 0, V(0)) == -1    # not a multiple of 16
+    assert P.bwta_probe_stream_read(V(A + 8), 64, V(A), 0, V(0)) == -1
+    assert P.bwta_probe_mfma(2, 1024, 10, V(A), V(0)) == -1           # unknown format
+    assert P.bwta_probe_mfma(0, 1022, 10, V(A), V(0)) == -1           # waves not in blocks of 4
 
 
 def test_version_and_sizes(L):
