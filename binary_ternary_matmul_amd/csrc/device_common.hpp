@@ -31,6 +31,38 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// The value of lane (lane ^ b) for b a power of two below 64 (b a compile-time
+// constant once the caller is unrolled): DPP quad permutes for bits 0 and 1,
+// the swizzle unit's xor mode (within 32 lanes) for bits 2 to 4, and a lane
+// permute for bit 5.  None needs a per-lane address.
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int b) {
+  switch (b) {
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+    case 4: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);
+    case 8: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x201F);
+    case 16: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+    default: return (uint32_t)__builtin_amdgcn_ds_bpermute((__lane_id() ^ b) << 2, (int)v);
+  }
+}
+__device__ __forceinline__ float xor_lane(float v, int b) {
+  return __uint_as_float(xor_lane(__float_as_uint(v), b));
+}
+__device__ __forceinline__ int xor_lane(int v, int b) { return (int)xor_lane((uint32_t)v, b); }
+
+// Buffer descriptor over [base, base + bytes) with range checking: a load at
+// or past `bytes` reads 0 and a store there is dropped.  The base goes through
+// readfirstlane so that the descriptor lives in SGPRs (the caller's base must
+// be wave-uniform).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t checked_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
+}
+
 // Pairwise tree over N (power of two) values held by one lane.
 template <int N>
 __device__ __forceinline__ float lane_tree(const float (&v)[N]) {
@@ -77,22 +109,22 @@ __device__ __forceinline__ float wave_tree(const float (&in)[N]) {
       const uint32_t lo_b = __float_as_uint(v[j]), up_b = __float_as_uint(v[j + cnt / 2]);
       const float keep = __uint_as_float((lo_b & ~hi) | (up_b & hi));
       const float send = __uint_as_float((up_b & ~hi) | (lo_b & hi));
-      const float recv = __shfl_xor(send, 1 << s, kWave);
+      const float recv = xor_lane(send, 1 << s);
       v[j] = keep + recv;
     }
   }
   float r = v[0];
 #pragma unroll
-  for (int b = s; b < 6; ++b) r = r + __shfl_xor(r, 1 << b, kWave);
+  for (int b = s; b < 6; ++b) r = r + xor_lane(r, 1 << b);
 #pragma unroll
-  for (int b = s - 1; b >= 0; --b) r = r + __shfl_xor(r, 1 << b, kWave);
+  for (int b = s - 1; b >= 0; --b) r = r + xor_lane(r, 1 << b);
   return r;
 }
 
 // Exact integer sum over the 64 lanes.
 __device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
-  for (int b = 0; b < 6; ++b) v += __shfl_xor(v, 1 << b, kWave);
+  for (int b = 0; b < 6; ++b) v += xor_lane(v, 1 << b);
   return v;
 }
 

@@ -66,18 +66,6 @@ constexpr int kMaxSU = 8;               // staged 16-byte units per thread and p
 constexpr uint32_t kOOB = 0x80000000u;  // an offset past every range check
 constexpr size_t kMaxLds = 150 * 1024;
 
-// Buffer descriptor with range checking over `bytes` (raw buffer: an offset
-// at or past `bytes` reads 0).  The base goes through readfirstlane so the
-// descriptor lives in SGPRs.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t checked_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t v = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
-                                           0x00020000);
-}
-
 // s_waitcnt immediate for "vmcnt = 0" (expcnt and lgkmcnt at their no-wait
 // maxima; vmcnt is split over bits 3:0 and 15:14).
 constexpr int vmcnt_wait0() { return 0x0F70; }

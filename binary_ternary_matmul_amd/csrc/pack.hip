@@ -63,6 +63,40 @@ __device__ __forceinline__ uint32_t neg_bit(uint32_t ux) {
   return (ux >> 31) & ((0x80000000u - ux) >> 31);
 }
 
+// bf16 pass 2 on packed 16-bit halves.  A run word holds elements 2q (low
+// half) and 2q+1 (high half).  A bf16 value widens to fp32 exactly (low 16 bits
+// zero), so for a finite non-negative threshold with fp32 bit pattern U,
+// |x| > thr  <=>  bits16(|x|) > U >> 16: one 16-bit subtraction per half decides
+// two elements, and its sign bit spread over the half is the keep mask.  Bit
+// 2q of the low half and bit 2q+1 of the high half collect the mask and the
+// sign bits; folding the halves gives the plane bytes.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void ternary_run_bf16(const uint32_t (&raw)[4], uint32_t t2, float& ksum,
+                                                 uint32_t& mb, uint32_t& sb, uint32_t& cnt) {
+  float kept[RUN];
+  uint32_t macc = 0, nacc = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t a = raw[q] & 0x7FFF7FFFu;  // |x| of both halves
+    const u16x2 d = __builtin_bit_cast(u16x2, t2) - __builtin_bit_cast(u16x2, a);
+    const uint32_t km = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, d) >> (int16_t)15);
+    const uint32_t kw = a & km;  // kept |x| (or +0) of both halves
+    kept[2 * q] = __uint_as_float(kw << 16);
+    kept[2 * q + 1] = __uint_as_float(kw & 0xFFFF0000u);
+    const uint32_t place = (1u << (2 * q)) | (2u << (16 + 2 * q));
+    macc |= km & place;
+    const u16x2 neg = __builtin_bit_cast(u16x2, raw[q]) >>
+                      u16x2{(uint16_t)(15 - 2 * q), (uint16_t)(14 - 2 * q)};
+    nacc |= __builtin_bit_cast(uint32_t, neg) & place;
+  }
+  ksum = lane_tree<RUN>(kept);
+  cnt = __builtin_popcount(macc);
+  mb = macc | (macc >> 16);
+  sb = mb & (nacc | (nacc >> 16));
+}
+
 __device__ __forceinline__ uint32_t raw_bits(float v) { return __float_as_uint(v); }
 __device__ __forceinline__ uint32_t raw_bits(uint16_t v) { return v; }
 
@@ -113,18 +147,54 @@ __device__ __forceinline__ void load_run(const T* __restrict__ row, int64_t e, i
   }
 }
 
+// The run of 8 elements at byte offset voff + soff of a row descriptor, with
+// 16-byte non-temporal buffer loads: a run past the descriptor's range reads
+// zeros (rows whose length is a multiple of 8 and 16-byte aligned, so a run is
+// wholly inside or wholly outside).
+constexpr int kNonTemporal = 2;  // buffer cache-policy bits: nt
+template <typename T>
+__device__ __forceinline__ void load_run_buf(__amdgpu_buffer_rsrc_t rs, int voff, int soff,
+                                             uint32_t (&raw)[Raw<T>::kWords]) {
+  constexpr int NW = Raw<T>::kWords;
+#pragma unroll
+  for (int v = 0; v < NW / 4; ++v) {
+    const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16 * v, soff, kNonTemporal);
+    raw[4 * v + 0] = u.x;
+    raw[4 * v + 1] = u.y;
+    raw[4 * v + 2] = u.z;
+    raw[4 * v + 3] = u.w;
+  }
+}
+
 template <int LPR>
 __device__ __forceinline__ float lanes_tree(float v) {
   // pairwise over the LPR lanes of one row (lane bit 0 first)
 #pragma unroll
-  for (int b = 1; b < LPR; b <<= 1) v = v + __shfl_xor(v, b, kWave);
+  for (int b = 1; b < LPR; b <<= 1) v = v + xor_lane(v, b);
   return v;
 }
 template <int LPR>
 __device__ __forceinline__ int lanes_sum(int v) {
 #pragma unroll
-  for (int b = 1; b < LPR; b <<= 1) v += __shfl_xor(v, b, kWave);
+  for (int b = 1; b < LPR; b <<= 1) v += xor_lane(v, b);
   return v;
+}
+
+// Root of the pairwise tree over the W (<= 16) per-wave values red[0 .. W) of a
+// row: lane q < W takes value q and lanes W .. 15 exact zeros (the zero
+// padding of the tree), a butterfly over lane bits 0 .. 3 pairs them in tree
+// order, and lane 0's root is returned to the whole wave.
+__device__ __forceinline__ float waves_tree(const float* red, int W, int lane) {
+  float v = lane < W ? red[lane] : 0.0f;
+#pragma unroll
+  for (int b = 1; b < 16; b <<= 1) v = v + xor_lane(v, b);
+  return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
+}
+__device__ __forceinline__ int waves_sum(const int* red, int W, int lane) {
+  int v = lane < W ? red[lane] : 0;
+#pragma unroll
+  for (int b = 1; b < 16; b <<= 1) v += xor_lane(v, b);
+  return __builtin_amdgcn_readfirstlane(v);
 }
 
 // RELOAD: pass 2 reads each run again (from L2: the block read it moments
@@ -144,7 +214,8 @@ pack_rows_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t sr, i
   __shared__ int red_cnt[16];
 
   const int lane = __lane_id();
-  const int wid = threadIdx.x / kWave;
+  // the wave index is wave-uniform: keep it (and what derives from it) scalar
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
   const int ll = lane % LPR;
   // rows handled by the block per iteration, and this lane's row among them
@@ -152,59 +223,92 @@ pack_rows_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t sr, i
   const int row_in_block = LPR == 64 ? wid / W : wid * RPW + lane / LPR;
   const int w_in_row = LPR == 64 ? wid - (wid / W) * W : 0;
   const float fK = (float)K;
+  const int Ki = (int)K;  // K <= 65536: offsets inside a row fit 32 bits
 
+  // wave-uniform: all GPW groups of this wave lie inside the row
+  const bool full = VEC && (w_in_row * GPW + GPW) * G <= Ki;
+  const int e0 = (w_in_row * GPW) * G + ll * RUN;
+  // Whole-wave rows with unit stride read through a per-row buffer descriptor
+  // and store the plane bytes through one: the descriptors' range checks stand
+  // in for every per-lane bounds test (the row's end, padding bytes, rows past
+  // the last), and the group offsets become constants.
+  constexpr bool BUF = LPR == 64 && VEC;
+  auto row_ptr = [&](int64_t r) { return X + (r < rows ? r : 0) * sr; };
+  auto fetch_from = [&](const T* xr, int i, uint32_t (&dst)[NW]) {
+    if constexpr (VEC) {
+      if (full)
+        load_run<T, 0>(xr, e0 + i * G, K, 1, dst);
+      else
+        load_run<T, 1>(xr, e0 + i * G, K, 1, dst);
+    } else {
+      load_run<T, 2>(xr, e0 + i * G, K, sk, dst);
+    }
+  };
+  // Groups that lie wholly past the end of the row hold only zero padding:
+  // their sums are exact zeros and they store nothing (wave-uniform).
+  auto in_row_g = [&](int i) { return full || (w_in_row * GPW + i) * G < Ki; };
+  auto fetch_row = [&](const T* xr, uint32_t (&dst)[GPW][NW]) {
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < GPW; ++i) load_run<T, 0>(xr, e0 + i * G, K, 1, dst[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < GPW; ++i) fetch_from(xr, i, dst[i]);
+    }
+  };
   for (int64_t r0 = (int64_t)blockIdx.x * rpb; r0 < rows; r0 += (int64_t)gridDim.x * rpb) {
     const int64_t r = r0 + row_in_block;
     const bool live = r < rows;
-    const T* xrow = X + (live ? r : 0) * sr;
+    const T* xrow = row_ptr(r);
+    const __amdgpu_buffer_rsrc_t xs = checked_rsrc(xrow, live ? Ki * (int)sizeof(T) : 0);
+    auto fetch = [&](int i, uint32_t (&dst)[NW]) {
+      if constexpr (BUF)
+        load_run_buf<T>(xs, e0 * (int)sizeof(T), i * G * (int)sizeof(T), dst);
+      else
+        fetch_from(xrow, i, dst);
+    };
 
     uint32_t raw[RELOAD ? 1 : GPW][NW];
-    // wave-uniform: all GPW groups of this wave lie inside the row
-    const bool full = VEC && (int64_t)(w_in_row * GPW + GPW) * G <= K;
-    const int64_t e0 = (int64_t)(w_in_row * GPW) * G + (int64_t)ll * RUN;
-    auto fetch = [&](int i, uint32_t (&dst)[NW]) {
-      if constexpr (VEC) {
-        if (full)
-          load_run<T, 0>(xrow, e0 + i * G, K, 1, dst);
-        else
-          load_run<T, 1>(xrow, e0 + i * G, K, 1, dst);
-      } else {
-        load_run<T, 2>(xrow, e0 + i * G, K, sk, dst);
-      }
-    };
     if constexpr (!RELOAD) {
-      if (full) {
+      if constexpr (BUF) {
 #pragma unroll
-        for (int i = 0; i < GPW; ++i) load_run<T, 0>(xrow, e0 + i * G, K, 1, raw[i]);
+        for (int i = 0; i < GPW; ++i)
+          if (in_row_g(i)) fetch(i, raw[i]);
       } else {
-#pragma unroll
-        for (int i = 0; i < GPW; ++i) fetch(i, raw[i]);
+        fetch_row(xrow, raw);
       }
     }
+
+    auto in_row = in_row_g;
 
     // Pass 1: tree(|x|).
     float part[GPW];
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
+      part[i] = 0.0f;
+      if (!in_row(i)) continue;
       if constexpr (RELOAD) fetch(i, raw[0]);
       const uint32_t* rw = raw[RELOAD ? 0 : i];
       float a[RUN];
 #pragma unroll
-      for (int j = 0; j < RUN; ++j) a[j] = __uint_as_float(ebits(rw, j, T{}) & 0x7FFFFFFFu);
+      for (int j = 0; j < RUN; ++j) a[j] = fabsf(__uint_as_float(ebits(rw, j, T{})));
       part[i] = lane_tree<RUN>(a);
     }
     float total;
     if constexpr (LPR == 64) {
       total = wave_tree<GPW>(part);
       if (W > 1) {
+        // The barriers here order LDS only: __syncthreads() would also wait for
+        // every global access of the wave in flight (the previous row's plane
+        // stores among them).
         if (lane == 0) red_sum[wid] = total;
-        __syncthreads();
-        total = tree16(&red_sum[row_in_block * W], W);
+        lds_barrier_local();
+        total = waves_tree(&red_sum[row_in_block * W], W, lane);
         // The binary rule has no second barrier in this iteration: without this
         // one a wave could store the next row's sum over red_sum while a slower
         // wave of the same row still reads it.  (The ternary rule's second
         // barrier below already separates the two.)
-        if constexpr (!TERNARY) __syncthreads();
+        if constexpr (!TERNARY) lds_barrier_local();
       }
     } else {
       total = lanes_tree<LPR>(part[0]);
@@ -224,12 +328,19 @@ pack_rows_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t sr, i
     }
     // Each lane stores its own byte of each plane (byte = (group*G + ll*8) / 8)
     // as soon as the group is done, so no per-group state outlives it.
-    const int64_t base = r * row_bytes;
+    const int64_t base = (live ? r : 0) * row_bytes;
+    const int boff = (w_in_row * GPW) * LPR + ll;  // this lane's byte of group 0
+    const uint32_t rb = live ? (uint32_t)row_bytes : 0u;
+    const __amdgpu_buffer_rsrc_t ms = checked_rsrc(TERNARY ? mask + base : sign + base, rb);
+    const __amdgpu_buffer_rsrc_t ss = checked_rsrc(sign + base, rb);
     auto store_bytes = [&](int i, uint32_t mb, uint32_t sb) {
-      const int64_t byte = (int64_t)(w_in_row * GPW + i) * LPR + ll;
-      if (live && byte < row_bytes) {
-        if constexpr (TERNARY) mask[base + byte] = (uint8_t)mb;
-        sign[base + byte] = (uint8_t)sb;
+      if constexpr (BUF) {
+        if constexpr (TERNARY)
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)mb, ms, boff, i * LPR, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, ss, boff, i * LPR, 0);
+      } else if (live && (full || boff + i * LPR < (int)row_bytes)) {
+        if constexpr (TERNARY) mask[base + boff + i * LPR] = (uint8_t)mb;
+        sign[base + boff + i * LPR] = (uint8_t)sb;
       }
     };
     float alpha_v;
@@ -238,24 +349,33 @@ pack_rows_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t sr, i
       const float mu = total / fK;
       const float thr = 0.5f * mu;
       const uint32_t uthr = __float_as_uint(thr);
+      const uint32_t t2 = (uthr >> 16) * 0x10001u;  // bf16 threshold in both halves
       // Pass 2: threshold, plane bytes, tree(kept |x|), nnz.
 #pragma unroll
       for (int i = 0; i < GPW; ++i) {
+        part[i] = 0.0f;
+        if (!in_row(i)) continue;
         if constexpr (RELOAD) fetch(i, raw[0]);
         const uint32_t* rw = raw[RELOAD ? 0 : i];
-        float kept[RUN];
         uint32_t mb = 0, sb = 0;
+        if constexpr (sizeof(T) == 2) {
+          uint32_t c;
+          ternary_run_bf16(raw[RELOAD ? 0 : i], t2, part[i], mb, sb, c);
+          count += c;
+        } else {
+          float kept[RUN];
 #pragma unroll
-        for (int j = 0; j < RUN; ++j) {
-          const uint32_t ux = ebits(rw, j, T{});
-          const uint32_t ua = ux & 0x7FFFFFFFu;          // |x|
-          const uint32_t keep = gt_bit(ua, uthr);        // |x| > thr
-          kept[j] = __uint_as_float(ua & (0u - keep));   // keep ? |x| : +0
-          mb |= keep << j;
-          sb |= (keep & (ux >> 31)) << j;                // kept and negative
+          for (int j = 0; j < RUN; ++j) {
+            const uint32_t ux = ebits(rw, j, T{});
+            const uint32_t ua = ux & 0x7FFFFFFFu;          // |x|
+            const uint32_t keep = gt_bit(ua, uthr);        // |x| > thr
+            kept[j] = __uint_as_float(ua & (0u - keep));   // keep ? |x| : +0
+            mb |= keep << j;
+            sb |= (keep & (ux >> 31)) << j;                // kept and negative
+          }
+          part[i] = lane_tree<RUN>(kept);
+          count += __builtin_popcount(mb);
         }
-        part[i] = lane_tree<RUN>(kept);
-        count += __builtin_popcount(mb);
         // Finish the group here: left alone, the compiler sinks the kept-value
         // trees past the store branches and holds every group's temporaries at
         // once (2048 x 11008 bf16: 118 VGPRs instead of 79).
@@ -272,10 +392,9 @@ pack_rows_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t sr, i
             red_kept[wid] = ktot;
             red_cnt[wid] = ctot;
           }
-          __syncthreads();
-          ktot = tree16(&red_kept[row_in_block * W], W);
-          ctot = 0;
-          for (int q = 0; q < W; ++q) ctot += red_cnt[row_in_block * W + q];
+          lds_barrier_local();
+          ktot = waves_tree(&red_kept[row_in_block * W], W, lane);
+          ctot = waves_sum(&red_cnt[row_in_block * W], W, lane);
         }
       } else {
         ktot = lanes_tree<LPR>(part[0]);
@@ -287,6 +406,7 @@ pack_rows_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t sr, i
       alpha_v = total / fK;
 #pragma unroll
       for (int i = 0; i < GPW; ++i) {
+        if (!in_row(i)) continue;
         if constexpr (RELOAD) fetch(i, raw[0]);
         const uint32_t* rw = raw[RELOAD ? 0 : i];
         uint32_t sb = 0;
@@ -587,11 +707,11 @@ struct Plan {
 };
 
 // Rows up to 4096 values: one wave per row (8 groups of 512 at most) and four
-// rows per block.  Longer rows: 4 groups per wave, up to 16 waves per row in
-// blocks of at most 512 or 1024 threads - fewer registers per wave and more waves
-// in flight than 8 groups (2048 x 11008 bf16: 25 us against 31 us), and no wave
-// that would hold only padding (11008: 6 waves, not 8).  Beyond 32768 values: 8
-// groups per wave that re-read their runs in pass 2.
+// rows per block.  Up to 16384 values: 8 groups per wave and as many waves per
+// row as hold data (11008: 3 waves, the last one partly padding, whose empty
+// groups are skipped), in blocks of at most 256 threads.  Up to 32768 values:
+// 4 groups per wave, up to 16 waves per row in blocks of 1024 threads.  Beyond:
+// 8 groups per wave that re-read their runs in pass 2.
 Plan plan_for(int64_t K) {
   Plan pl;
   if (K <= 16 * RUN) return {16, 1, 1, 256, 256};
@@ -604,9 +724,12 @@ Plan plan_for(int64_t K) {
     pl.gpw = (int)p;
     pl.W = 1;
     pl.block = pl.bound = 256;
+  } else if (p <= 32) {
+    pl.gpw = 8;
+    pl.bound = 256;
   } else if (p <= 64) {
     pl.gpw = 4;
-    pl.bound = p <= 32 ? 512 : 1024;
+    pl.bound = 1024;
   } else {
     pl.gpw = 8;
     pl.bound = 1024;
@@ -640,11 +763,10 @@ hipError_t launch_rows(const T* X, int64_t rows, int64_t K, int64_t sr, int64_t 
       case 4: BWTA_ROWS(4, 64, 256, false); break;
       default: BWTA_ROWS(8, 64, 256, false); break;
     }
+  } else if (pl.gpw == 8 && pl.bound == 256) {
+    BWTA_ROWS(8, 64, 256, false);
   } else if (pl.gpw == 4) {
-    if (pl.bound == 512)
-      BWTA_ROWS(4, 64, 512, false);
-    else
-      BWTA_ROWS(4, 64, 1024, false);
+    BWTA_ROWS(4, 64, 1024, false);
   } else {
     BWTA_ROWS(8, 64, 1024, true);
   }

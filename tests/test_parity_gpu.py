@@ -76,6 +76,31 @@ def test_ternarize_pack(bw, oracle, M, K, bf16):
     assert (to_host(got.alpha).view(np.uint32) == alpha.view(np.uint32)).all()
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("K", [8, 4096, 11008, 65536])
+def test_ternarize_pack_ties(bw, oracle, K, bf16):
+    """Magnitudes equal to the threshold are dropped (|x| > thr keeps).  Each run
+    of 8 is (2, 1.5, t, t, 0, 0, 0, 0) with t = 0.25 and signs varied, so every
+    row sums exactly to K/2, mu = 0.5 and thr = 0.25 = t; rows scaled by powers
+    of two keep the tie."""
+    run = np.array([2.0, 1.5, 0.25, 0.25, 0.0, 0.0, 0.0, 0.0])
+    rows = []
+    for r in range(6):
+        v = np.tile(run, K // 8) * 2.0 ** (r - 3)
+        sgn = np.where((np.arange(K) * 7 + r) % 3 == 0, -1.0, 1.0)
+        rows.append(v * sgn)
+    x = np.array(rows, np.float32)
+    if bf16:
+        x = (x.view(np.uint32) >> 16).astype(np.uint16)
+    got = bw.bwta_ternarize_pack(to_dev(x))
+    t, alpha, nnz = oracle.ternarize(x)
+    assert (nnz == 2 * (K // 8)).all(), "ties must be dropped"
+    assert (to_host(got.mask) == oracle.pack_plane(t, "mask")).all()
+    assert (to_host(got.sign) == oracle.pack_plane(t, "sign")).all()
+    assert (to_host(got.nnz) == nnz).all()
+    assert (to_host(got.alpha).view(np.uint32) == alpha.view(np.uint32)).all()
+
+
 def test_ternarize_pack_row_stride(bw, oracle):
     import torch
     x = _x(5, 40, 300, False)
