@@ -204,13 +204,22 @@ __device__ __forceinline__ v16f mfma_fp4(v4i a, v4i b, v16f c) {
 // rows, 64 KiB in all (within the rings whenever S > 1).
 constexpr size_t kXchgBytes = (size_t)TILES * TILES * 16 * kWave * 4;
 
+// Two fp32 values as a bf16 pair (low half first), each rounded to nearest
+// even: one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
 // Store row block i (32 rows x 32 NJ columns) of a complete tile from the
-// lanes' output words o[j][qh][0..3] (row r, columns 32 j + 8 qh + 4 g + 0..3;
-// ES-byte elements, bf16 pairs packed per 32-bit word on the way).  In that layout
-// a store instruction covers 32 rows x 4 elements, one L2 request per row, so the
-// block goes through LDS (stg: the wave's own, free staging area) row-major, and
-// each 16-byte store instruction then writes whole rows: 64 lanes x 16 bytes
-// over 64 lanes / (2 NJ ES) rows, a quarter to an eighth of the requests.
+// lanes' output words o[j][qh][..] (row r, columns 32 j + 8 qh + 4 g + 0..3;
+// ES = 4: one fp32 or int32 per word, ES = 2: bf16 pairs in words 0 and 1).
+// In that layout a store instruction covers 32 rows x 4 elements, one L2
+// request per row, so the block goes through LDS (stg: the wave's own, free
+// staging area) row-major, and each 16-byte store instruction then writes whole
+// rows: 64 lanes x 16 bytes over 64 lanes / (2 NJ ES) rows, a quarter to an
+// eighth of the requests.
 template <int NJ, int ES>
 __device__ __forceinline__ void store_row_block(const uint32_t (&o)[TILES][4][4], uint8_t* stg,
                                                 int r, int g, int lane,
@@ -230,7 +239,7 @@ __device__ __forceinline__ void store_row_block(const uint32_t (&o)[TILES][4][4]
       if constexpr (ES == 4)
         *reinterpret_cast<v4u*>(dst) = v4u{w[0], w[1], w[2], w[3]};
       else
-        *reinterpret_cast<v2u*>(dst) = v2u{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+        *reinterpret_cast<v2u*>(dst) = v2u{w[0], w[1]};
     }
   // other lanes read what this lane wrote: complete the writes first
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -662,17 +671,22 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
 #pragma unroll
       for (int jj = 0; jj < TILES / 2; ++jj)
 #pragma unroll
-        for (int qh = 0; qh < 4; ++qh)
+        for (int qh = 0; qh < 4; ++qh) {
+          float y[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const float y1 = acc[ii][2 * jj][4 * qh + u] * (aa * ab2[2 * jj][qh][u]);
             const float y2 = acc[ii][2 * jj + 1][4 * qh + u] * (aa * ab2[2 * jj + 1][qh][u]);
-            const float y = y1 + y2;
-            if constexpr (OUT == (int)Elt::F32)
-              o[jj][qh][u] = __float_as_uint(y);
-            else
-              o[jj][qh][u] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y);
+            y[u] = y1 + y2;
           }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if constexpr (OUT == (int)Elt::F32)
+              o[jj][qh][u] = __float_as_uint(y[u]);
+            else if (u < 2)
+              o[jj][qh][u] = pack_bf16x2(y[2 * u], y[2 * u + 1]);
+          }
+        }
       if (full) {
         store_row_block<TILES / 2, ES>(o, stg, r, g, lane, yrs, ldb, i);
       } else if (row < m_valid) {
@@ -688,7 +702,7 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
                 if constexpr (ES == 4)
                   *reinterpret_cast<uint32_t*>(yp) = o[jj][qh][u];
                 else
-                  *reinterpret_cast<uint16_t*>(yp) = (uint16_t)o[jj][qh][u];
+                  *reinterpret_cast<uint16_t*>(yp) = (uint16_t)(o[jj][qh][u >> 1] >> (16 * (u & 1)));
               }
             }
       }
@@ -707,17 +721,24 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
 #pragma unroll
     for (int j = 0; j < TILES; ++j)
 #pragma unroll
-      for (int qh = 0; qh < 4; ++qh)
+      for (int qh = 0; qh < 4; ++qh) {
+        if constexpr (OUT == (int)Elt::BF16) {
+          float y[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float a = acc[ii][j][4 * qh + u];
-          if constexpr (OUT == (int)Elt::I32)
-            o[j][qh][u] = (uint32_t)(int)a;
-          else if constexpr (OUT == (int)Elt::F32)
-            o[j][qh][u] = __float_as_uint(a * (aa * ab[j][qh][u]));
-          else
-            o[j][qh][u] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(a * (aa * ab[j][qh][u])));
+          for (int u = 0; u < 4; ++u) y[u] = acc[ii][j][4 * qh + u] * (aa * ab[j][qh][u]);
+          o[j][qh][0] = pack_bf16x2(y[0], y[1]);
+          o[j][qh][1] = pack_bf16x2(y[2], y[3]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float a = acc[ii][j][4 * qh + u];
+            if constexpr (OUT == (int)Elt::I32)
+              o[j][qh][u] = (uint32_t)(int)a;
+            else
+              o[j][qh][u] = __float_as_uint(a * (aa * ab[j][qh][u]));
+          }
         }
+      }
     if (full) {
       store_row_block<TILES, ES>(o, stg, r, g, lane, yrs, ldb, i);
     } else if (row < m_valid) {
@@ -733,7 +754,7 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
               if constexpr (ES == 4)
                 *reinterpret_cast<uint32_t*>(yp) = o[j][qh][u];
               else
-                *reinterpret_cast<uint16_t*>(yp) = (uint16_t)o[j][qh][u];
+                *reinterpret_cast<uint16_t*>(yp) = (uint16_t)(o[j][qh][u >> 1] >> (16 * (u & 1)));
             }
           }
     }
