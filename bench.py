@@ -123,6 +123,27 @@ def profiled_traffic(key):
     return None
 
 
+def probe_read_us(x, reps=20):
+    """Time of the read-only stream probe over the bytes of device tensor x, read
+    again and again (as a benchmark loop re-reads the same input)."""
+    import ctypes
+    import torch
+    from binary_ternary_matmul_amd import build
+    P = ctypes.CDLL(build.PROBE_LIB)
+    V = ctypes.c_void_p
+    P.bwta_probe_stream_read.argtypes = [V, ctypes.c_size_t, V, ctypes.c_int, V]
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    nb = x.numel() * x.element_size() // 16 * 16
+    # the stream is read inside the call: time_calls captures on its own stream
+    best = None
+    for blocks in (0, 1024, 2048, 4096):
+        ms = time_calls(lambda blocks=blocks: P.bwta_probe_stream_read(
+            V(x.data_ptr()), nb, V(sink.data_ptr()), blocks,
+            V(torch.cuda.current_stream().cuda_stream)), reps=reps)
+        best = ms if best is None else min(best, ms)
+    return best * 1e3
+
+
 def ceilings(copies=24):
     """The chip's measured ceilings (libbwta_probe.so): read-only HBM streams of
     one decode weight's size (29.59 MB, each launch reading another of `copies`
@@ -143,15 +164,20 @@ def ceilings(copies=24):
     for b in bufs:
         b.fill_(1)
 
-    def small():
+    # The grid is swept (0 = one round of loads per thread) and the fastest kept.
+    grids = (0, 1024, 2048, 4096)
+
+    def small(blocks):
         for b in bufs:
-            assert P.bwta_probe_stream_read(V(b.data_ptr()), nb, V(sink.data_ptr()), 0, st()) == 0
-    ms = time_calls(small, reps=2) / copies
+            assert P.bwta_probe_stream_read(V(b.data_ptr()), nb, V(sink.data_ptr()), blocks,
+                                            st()) == 0
+    ms = min(time_calls(lambda g=g: small(g), reps=2) for g in grids) / copies
     out["hbm_read_29.6MB_GBps"] = round(nb / (ms * 1e-3) / 1e9, 1)
     del bufs
     big = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
-    ms = time_calls(lambda: P.bwta_probe_stream_read(V(big.data_ptr()), big.numel(),
-                                                       V(sink.data_ptr()), 0, st()), reps=3)
+    ms = min(time_calls(lambda g=g: P.bwta_probe_stream_read(V(big.data_ptr()), big.numel(),
+                                                              V(sink.data_ptr()), g, st()), reps=3)
+             for g in (0, 2048, 4096, 8192))
     out["hbm_read_1GiB_GBps"] = round(big.numel() / (ms * 1e-3) / 1e9, 1)
     del big
     for fmt, name, per in ((0, "fp4_mfma_loop_TOPS", 131072), (1, "int8_mfma_loop_TOPS", 65536)):
@@ -213,8 +239,28 @@ def bench_prefill(bw, steps, warmup, M=2048):
         per_gemm[lin.name] = {"M": M, "N": lin.N, "K": lin.K, "us": round(ms * 1e3, 2),
                               "tops": round(2.0 * M * lin.N * lin.K / (ms * 1e-3) / 1e12, 1)}
     tern_ms = time_calls(ternarize_all, reps=steps)
+    # Ternarize roofline (HBM-bound): each input's bf16 rows read once, both
+    # planes and the per-row alpha and nnz written once.
+    tern = {}
+    tern_bytes = 0
+    for name, x in X.items():
+        rows, K = x.shape
+        nb = rows * K * x.element_size() + rows * (2 * bw.row_bytes(K) + 8)
+        tern_bytes += nb
+        ms = time_calls(lambda x=x: bw.bwta_ternarize_pack(x), reps=steps)
+        tern[name] = {"rows": rows, "K": K, "us": round(ms * 1e3, 2), "bytes": nb,
+                      "GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
+    tern_gbs = tern_bytes / (tern_ms * 1e-3) / 1e9
+    tern_roof = {"bound": "hbm", "kernel": "pack_rows_kernel", "achieved": round(tern_gbs, 1),
+                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(tern_gbs / HBM_PEAK_GBS, 3),
+                 "bytes_per_step": tern_bytes, "traffic": None, "per_input": tern}
+    trs = [profiled_traffic(f"pack_rows_kernel.ternarize.K{t['K']}") for t in tern.values()]
+    if all(trs):
+        tern_roof["traffic"] = sum(t["bytes"] for t in trs)
+        tern_roof["traffic_source"] = trs[0]["summary"]
     return dict(ops=ops, ms_step=ms_step, wall_ms_step=wall * 1e3 / steps, gemm_ms=gemm_ms,
-                ternarize_ms=tern_ms, per_gemm=per_gemm, lins=lins, X=X, W=W, M=M)
+                ternarize_ms=tern_ms, ternarize_roofline=tern_roof, per_gemm=per_gemm, lins=lins,
+                X=X, W=W, M=M)
 
 
 def bench_algo(bw, pre, algo, reps=5):
@@ -658,6 +704,7 @@ def main():
                    "ops_per_step": pre["ops"]},
         "gemm_frac_of_int8_peak": round(achieved / INT8_PEAK_TOPS, 3),
         "ternarize_us_per_step": round(pre["ternarize_ms"] * 1e3, 1),
+        "ternarize_roofline": pre["ternarize_roofline"],
         "host_wall_ms_per_step": round(pre["wall_ms_step"], 4),
         "per_gemm": pre["per_gemm"],
         "roofline": {"bound": "mfma", "kernel": "gemm_mfma_kernel", "achieved": round(achieved, 1),
@@ -672,6 +719,11 @@ def main():
     if not args.quick:
         log("[bench] ceilings (probe kernels)")
         line["ceilings"] = ceilings()
+        # the ternarize inputs' bytes through the pure read stream, for scale
+        for name, x in pre["X"].items():
+            t = line["ternarize_roofline"]["per_input"][name]
+            t["read_probe_us"] = round(probe_read_us(x), 2)
+            t["time_vs_read_probe"] = round(t["us"] / t["read_probe_us"], 2)
         fp4_loop = line["ceilings"]["fp4_mfma_loop_TOPS"]
         line["roofline"]["measured_peak"] = fp4_loop
         line["roofline"]["frac_of_measured_peak"] = round(achieved / fp4_loop, 3)
