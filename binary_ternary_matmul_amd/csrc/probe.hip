@@ -14,21 +14,24 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// 16-byte non-temporal loads, kPer per thread issued back to back (load j of
-// a thread at index base + j * stride, so every load instruction of a wave is
-// one contiguous 1 KiB); rounds of kPer * stride until the buffer is read.
+// 16-byte non-temporal loads: a wave reads kPer consecutive 1 KiB chunks (one
+// chunk per load instruction, lane l at byte 16 l of the chunk), all issued
+// before any is used, then moves on by the grid's span of chunks.
 constexpr int kPer = 8;
 
 __global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* __restrict__ buf,
                                                           size_t n16, uint32_t* __restrict__ sink) {
   __shared__ uint32_t red[256];
-  const size_t stride = (size_t)gridDim.x * 256;
+  const int lane = threadIdx.x & 63;
+  const size_t nchunks = (n16 + 63) / 64;
+  const size_t wave = (size_t)blockIdx.x * 4 + threadIdx.x / 64;
+  const size_t span = (size_t)gridDim.x * 4 * kPer;  // chunks per round of the grid
   uint32_t x = 0;
-  for (size_t base = (size_t)blockIdx.x * 256 + threadIdx.x; base < n16; base += kPer * stride) {
+  for (size_t c0 = wave * kPer; c0 < nchunks; c0 += span) {
     u32x4 v[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const size_t i = base + (size_t)j * stride;
+      const size_t i = (c0 + j) * 64 + lane;
       v[j] = i < n16 ? __builtin_nontemporal_load(buf + i) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
@@ -95,8 +98,9 @@ extern "C" int bwta_probe_stream_read(const void* buf, size_t bytes, uint32_t* s
   if (!buf || !sink || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(buf) % 16) != 0 ||
       blocks < 0)
     return -1;
-  if (blocks == 0) {  // one round of kPer loads per thread, at most 8192 blocks
-    const size_t need = (bytes / 16 + (size_t)256 * kPer - 1) / ((size_t)256 * kPer);
+  if (blocks == 0) {  // one round of kPer chunks per wave, at most 8192 blocks
+    const size_t chunks = (bytes / 16 + 63) / 64;
+    const size_t need = (chunks + 4 * kPer - 1) / (4 * kPer);
     blocks = need < 1 ? 1 : need > 8192 ? 8192 : (int)need;
   }
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0,

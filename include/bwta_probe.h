@@ -21,11 +21,12 @@ extern "C" {
 #endif
 
 /* Read `bytes` bytes of `buf` (16-byte aligned, bytes a multiple of 16) once
- * with 16-byte non-temporal loads spread over the whole chip (8 per thread in
- * flight at once), and store one 32-bit XOR of what each block read to
- * sink[block] (sink: blocks words; blocks = 0 picks one round of loads per
- * thread for buffers up to 32 MiB and 8192 blocks above).  Timing it gives the read-only HBM bandwidth of a
- * stream of that size. */
+ * with 16-byte non-temporal loads spread over the whole chip (each wave of a
+ * 256-thread block reads 8 consecutive KiB at a time, all loads in flight at
+ * once), and store one 32-bit XOR of what each block read to sink[block]
+ * (sink: blocks words, blocks <= 8192; blocks = 0 picks one round per wave, at
+ * most 8192 blocks).  Timing it gives the read-only HBM bandwidth of a stream of
+ * that size. */
 int bwta_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks,
                            void* stream);
 
