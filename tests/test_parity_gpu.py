@@ -59,9 +59,13 @@ def assert_close_f32(got, ref):
 # ----------------------------------------------------------------------------
 # ternarize_pack
 # ----------------------------------------------------------------------------
+# Row widths cover every launch plan of the row kernel: 16- and 32-lane rows,
+# one wave of 1-8 groups, 8 groups on 2-4 waves (a partial last wave, K not a
+# multiple of 8 on the element path, exactly 4 full waves), 4 groups on up to 16
+# waves, and 8 re-reading groups on 16 waves.
 TERN_SHAPES = [(1, 1), (3, 3), (5, 64), (7, 65), (9, 100), (33, 128), (17, 256), (16, 768),
-               (12, 1000), (8, 2048), (6, 3072), (5, 4096), (4, 4097), (3, 11008), (2, 28672),
-               (2, 65536)]
+               (12, 1000), (8, 2048), (6, 3072), (5, 4096), (4, 4097), (5, 6000), (3, 11008),
+               (3, 12345), (2, 16384), (2, 16392), (2, 28672), (2, 65536)]
 
 
 @pytest.mark.parametrize("bf16", [False, True])
@@ -119,7 +123,7 @@ def test_ternarize_pack_row_stride(bw, oracle):
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("N,K", [(1, 1), (3, 7), (70, 64), (33, 100), (130, 768), (9, 4096),
-                                 (5, 11008), (3, 28672)])
+                                 (5, 11008), (4, 12345), (3, 28672)])
 def test_pack_weights(bw, oracle, N, K, bf16):
     w = _w(N * 31 + K, N, K, bf16)
     got = bw.bwta_pack_weights(to_dev(w))
