@@ -613,8 +613,9 @@ def calibrate_copy(nbytes=256 << 20, reps=3):
 
 
 def profile_gemv(bw, copies=4):
-    """A few cold launches of each decode shape, and of gate/up stacked into one
-    [57344, 8192] weight (for profiler counters)."""
+    """A few cold launches of each decode shape, of gate/up stacked into one
+    [57344, 8192] weight, and (M = 1) of the fused decode call (for profiler
+    counters)."""
     import torch
     from binary_ternary_matmul_amd import inputs
     up = None
@@ -639,6 +640,12 @@ def profile_gemv(bw, copies=4):
                     bw.bwta_gemv(a, wi, "f32", "auto", y2)
                 torch.cuda.synchronize()
                 del fs
+            if M == 1:  # the decode linear in one launch, bf16 row in
+                X = dev(lin.x())
+                torch.cuda.synchronize()
+                for wi in ws:
+                    bw.bwta_gemv_fused(X, wi, "f32", y)
+                torch.cuda.synchronize()
             del ws, w
     print(json.dumps({"profile_gemv": "done", "copies": copies}), flush=True)
 

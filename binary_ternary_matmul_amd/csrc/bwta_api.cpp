@@ -373,6 +373,10 @@ bwta_status bwta_gemv_fused(const void* X, bwta_dtype x_dtype, int64_t ldx, cons
     g.ws = workspace;
     g.ws_bytes = ws_bytes;
   }
+  // One row: the popcount decode kernel with the ternarization in each block.
+  const hipError_t e = bwta::launch_gemv_fused_row(g, X, elt(x_dtype), a_mask, a_sign, a_alpha,
+                                                   a_nnz, static_cast<hipStream_t>(stream));
+  if (e != hipErrorNotSupported) return from_hip(e, "bwta_gemv_fused launch");
   return from_hip(bwta::launch_gemv_fused(g, X, elt(x_dtype), ldx, a_mask, a_sign, a_alpha, a_nnz,
                                           static_cast<hipStream_t>(stream)),
                   "bwta_gemv_fused launch");

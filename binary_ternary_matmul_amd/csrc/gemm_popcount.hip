@@ -294,6 +294,299 @@ gemv_popcount_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restri
   }
 }
 
+// Decode linear of ONE activation row in one launch (bwta_gemv_fused, M = 1):
+// every block ternarizes the row itself into LDS planes, then its waves stream
+// weight rows exactly as gemv_popcount_kernel does.  Each thread loads its share
+// of the row first; the wave's first weight loads go out as soon as that share
+// is in, so the rest of the ternarization runs under them.  Every block repeats
+// the ternarization, so blocks are as wide as the grid allows (WB = 4, 8 or 16
+// waves): the repeated work scales with the number of blocks.
+//
+// The block's ternarization follows the definition's tree: thread t < NT owns
+// the aligned range [t V, t V + V) of the row zero-padded to P = 2^ceil(log2 K)
+// (NT = min(64 WB, P / 8), V = P / NT), sums its runs of 8 in a pairwise tree,
+// and the 64 WB thread sums (zeros past NT) meet in a butterfly over the lanes
+// and a tree over the WB waves - all aligned sub-trees of the row's tree, so
+// mu, thr, the kept-value tree, nnz and alpha_a equal bwta_ternarize_pack's bit
+// for bit.  The row stays in registers between the two passes; pass 2 writes
+// the plane bytes into LDS.
+constexpr int kFusedMaxK = 32768;  // runs per thread <= 16 (bf16; fp32 rows up to 16384: <= 8)
+constexpr int kFusedPlaneBytes = kFusedMaxK / 8;
+constexpr int64_t kFusedRowWaves = 8192;  // grid cap (32 waves per compute unit)
+constexpr int64_t kFusedCUs = 256;
+
+template <typename TX>
+struct RowRun {
+  static constexpr int kWords = 8 * (int)sizeof(TX) / 4;  // 32-bit words per run of 8
+};
+
+// Raw words of the run at byte offset `off` of the row (K a multiple of 8: a run
+// is wholly in or out of the row; out of range, or off < 0, reads zeros).
+// Buffer loads with no branch around them, so the wait for the row's runs does
+// not also wait for the weight loads issued after them.
+template <typename TX>
+__device__ __forceinline__ void load_row_run(__amdgpu_buffer_rsrc_t xrs, int off,
+                                             uint32_t (&w)[RowRun<TX>::kWords]) {
+  constexpr int NW = RowRun<TX>::kWords;
+  const int o = off < 0 ? 0x40000000 : off;
+#pragma unroll
+  for (int v = 0; v < NW / 4; ++v) {
+    const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(xrs, o + 16 * v, 0, 0);
+    w[4 * v + 0] = u.x;
+    w[4 * v + 1] = u.y;
+    w[4 * v + 2] = u.z;
+    w[4 * v + 3] = u.w;
+  }
+}
+
+template <typename TX>
+__device__ __forceinline__ void row_run_values(const uint32_t (&w)[RowRun<TX>::kWords], float (&v)[8]) {
+  if constexpr (sizeof(TX) == 2) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(w[j]);
+  }
+}
+
+// Root of the block's tree over its WB waves' threads' values (thread order).
+template <int WB>
+__device__ __forceinline__ float block_tree(float v, float* red) {
+  const int lane = __lane_id(), wid = threadIdx.x / kWave;
+#pragma unroll
+  for (int b = 0; b < 6; ++b) v = v + xor_lane(v, 1 << b);
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float w[WB];
+#pragma unroll
+  for (int i = 0; i < WB; ++i) w[i] = red[i];
+  __syncthreads();
+  return lane_tree<WB>(w);
+}
+template <int WB>
+__device__ __forceinline__ int block_sum(int v, int* ired) {
+  const int lane = __lane_id(), wid = threadIdx.x / kWave;
+#pragma unroll
+  for (int b = 0; b < 6; ++b) v += xor_lane(v, 1 << b);
+  if (lane == 0) ired[wid] = v;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < WB; ++i) r += ired[i];
+  __syncthreads();
+  return r;
+}
+
+template <int NCH, typename TX, int OUT, int RUNS, int WB>
+__global__ void __launch_bounds__(WB * 64)
+gemv_fused_row_kernel(const TX* __restrict__ X, int K, const uint8_t* __restrict__ w_sign,
+                      const float* __restrict__ w_alpha, int64_t N, int64_t row_bytes,
+                      void* __restrict__ Y, uint8_t* __restrict__ o_mask,
+                      uint8_t* __restrict__ o_sign, float* __restrict__ o_alpha,
+                      int32_t* __restrict__ o_nnz) {
+  constexpr int R = 4;  // weight rows per wave and iteration, as in gemv_popcount_kernel
+  __shared__ __attribute__((aligned(16))) uint8_t s_mask[kFusedPlaneBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sign[kFusedPlaneBytes];
+  __shared__ float red[WB];
+  __shared__ int ired[WB];
+  const int lane = __lane_id();
+  const int t = threadIdx.x;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + t) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
+
+  // 1. the row's runs of this thread (RUNS >= its runs)
+  constexpr int NWR = RowRun<TX>::kWords;
+  int P = 8;
+  while (P < K) P <<= 1;
+  const int NT = P / 8 < WB * kWave ? P / 8 : WB * kWave;
+  const int V = P / NT;
+  const int runs = V / 8;  // a power of two <= RUNS
+  const bool part = t < NT;
+  const __amdgpu_buffer_rsrc_t xrs = checked_rsrc(X, (uint32_t)K * (uint32_t)sizeof(TX));
+  uint32_t xr[RUNS][NWR];
+#pragma unroll
+  for (int r = 0; r < RUNS; ++r)
+    load_row_run<TX>(xrs, part && r < runs ? (t * V + 8 * r) * (int)sizeof(TX) : -1, xr[r]);
+  // A lane's chunk past the row end loads the row's first bytes instead: its
+  // activation words are zero there, so those weight bits count nothing.
+  bool cvalid[NCH];
+  int64_t coff[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    cvalid[c] = (int64_t)c * 1024 + lane * 16 < row_bytes;
+    coff[c] = cvalid[c] ? (int64_t)c * 1024 + lane * 16 : 0;
+  }
+  u32x4 w[R][NCH];
+  auto load_w = [&](int64_t n0) {  // rows past N re-read row N - 1; nothing stores them
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int64_t n = n0 + r < N ? n0 + r : N - 1;
+        w[r][c] = load_nt16(w_sign + n * row_bytes + coff[c]);
+      }
+  };
+
+  // 2. ternarize the row into the LDS planes; the weight loads go out once the
+  // row's runs are in (issued earlier, they would queue ahead of other waves' row
+  // reads and hold up every block's ternarization)
+  float rs[RUNS];
+#pragma unroll
+  for (int r = 0; r < RUNS; ++r) {  // runs past `runs` hold zeros: exact zero sums
+    float v[8];
+    row_run_values<TX>(xr[r], v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = fabsf(v[j]);
+    rs[r] = lane_tree<8>(v);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(wave * R);
+  for (int i = t; i < (int)(row_bytes / 4); i += blockDim.x) {
+    reinterpret_cast<uint32_t*>(s_mask)[i] = 0u;
+    reinterpret_cast<uint32_t*>(s_sign)[i] = 0u;
+  }
+  const float total = block_tree<WB>(lane_tree<RUNS>(rs), red);
+  const float thr = 0.5f * (total / (float)K);
+  int cnt = 0;
+#pragma unroll
+  for (int r = 0; r < RUNS; ++r) {
+    rs[r] = 0.0f;
+    if (part && r < runs) {
+      float v[8], kept[8];
+      row_run_values<TX>(xr[r], v);
+      uint32_t mb = 0, sb = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float a = fabsf(v[j]);
+        const bool keep = a > thr;
+        kept[j] = keep ? a : 0.0f;
+        mb |= (uint32_t)keep << j;
+        sb |= (uint32_t)(keep && v[j] < 0.0f) << j;
+      }
+      rs[r] = lane_tree<8>(kept);
+      cnt += __builtin_popcount(mb);
+      const int byte = (t * V + 8 * r) / 8;
+      if (byte < (int)row_bytes) {
+        s_mask[byte] = (uint8_t)mb;
+        s_sign[byte] = (uint8_t)sb;
+      }
+    }
+  }
+  const float ktot = block_tree<WB>(lane_tree<RUNS>(rs), red);  // its barriers order the plane bytes
+  const int nnz = block_sum<WB>(cnt, ired);
+  const float alpha = nnz ? ktot / (float)nnz : 0.0f;
+  if (blockIdx.x == 0) {
+    if (o_mask)
+      for (int i = t; i < (int)row_bytes; i += blockDim.x) {
+        o_mask[i] = s_mask[i];
+        o_sign[i] = s_sign[i];
+      }
+    if (o_alpha && t == 0) {
+      o_alpha[0] = alpha;
+      o_nnz[0] = nnz;
+    }
+  }
+
+  // 3. the lane's activation words: p = mask ^ sign, s = sign
+  uint32_t ap[NCH][4], as[NCH][4];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int off = c * 1024 + lane * 16;
+    u32x4 mm = u32x4{0, 0, 0, 0}, ss = u32x4{0, 0, 0, 0};
+    if (cvalid[c]) {
+      mm = *reinterpret_cast<const u32x4*>(s_mask + off);
+      ss = *reinterpret_cast<const u32x4*>(s_sign + off);
+    }
+    ap[c][0] = mm.x ^ ss.x; ap[c][1] = mm.y ^ ss.y; ap[c][2] = mm.z ^ ss.z; ap[c][3] = mm.w ^ ss.w;
+    as[c][0] = ss.x; as[c][1] = ss.y; as[c][2] = ss.z; as[c][3] = ss.w;
+  }
+
+  // 4. the weight stream (acc = nnz - 2 sum popc(bfi(w, mask ^ sign, sign)))
+  for (int64_t n0 = wave * R; n0 < N; n0 += nwaves * R) {
+    if (n0 != wave * R) load_w(n0);
+    int c4[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) c4[r] = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t ww[4] = {w[r][c].x, w[r][c].y, w[r][c].z, w[r][c].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          c4[r] += __builtin_popcount((ww[q] & ap[c][q]) | (~ww[q] & as[c][q]));
+      }
+    wave_reduce_scatter_int<R>(c4);
+    if (lane < R) {
+      const int r = bitrev<2>(lane);
+      const int64_t n = n0 + r;
+      if (n < N) store_out<OUT>(Y, n, nnz - 2 * c4[0], alpha, OUT == (int)Elt::I32 ? 0.0f : w_alpha[n]);
+    }
+  }
+}
+
+template <int NCH, typename TX, int RUNS, int WB>
+hipError_t launch_fused_row_nch(const GemmArgs& g, const TX* X, uint8_t* o_mask, uint8_t* o_sign,
+                                float* o_alpha, int32_t* o_nnz, hipStream_t stream) {
+  const int64_t row_bytes = (g.K + 63) / 64 * 8;
+  const int64_t waves_needed = (g.N + 3) / 4;
+  int64_t blocks = (waves_needed + WB - 1) / WB;
+  if (blocks > kFusedRowWaves / WB) blocks = kFusedRowWaves / WB;
+  const dim3 grid((unsigned)blocks), block(WB * kWave);
+  switch (g.y_dt) {
+    case Elt::F32:
+      hipLaunchKernelGGL((gemv_fused_row_kernel<NCH, TX, (int)Elt::F32, RUNS, WB>), grid, block, 0, stream,
+                         X, (int)g.K, g.b_sign, g.b_alpha, g.N, row_bytes, g.Y, o_mask, o_sign,
+                         o_alpha, o_nnz);
+      break;
+    case Elt::BF16:
+      hipLaunchKernelGGL((gemv_fused_row_kernel<NCH, TX, (int)Elt::BF16, RUNS, WB>), grid, block, 0,
+                         stream, X, (int)g.K, g.b_sign, g.b_alpha, g.N, row_bytes, g.Y, o_mask, o_sign,
+                         o_alpha, o_nnz);
+      break;
+    default:
+      hipLaunchKernelGGL((gemv_fused_row_kernel<NCH, TX, (int)Elt::I32, RUNS, WB>), grid, block, 0, stream,
+                         X, (int)g.K, g.b_sign, g.b_alpha, g.N, row_bytes, g.Y, o_mask, o_sign,
+                         o_alpha, o_nnz);
+  }
+  return hipGetLastError();
+}
+
+// Every block ternarizes the whole row, so the redundant ternarization work
+// scales with the number of blocks: the launch takes the widest blocks (16, 8
+// or 4 waves) that still give every compute unit a block, with at most
+// kFusedRowWaves waves in the grid.  Threads hold RUNS runs of 8 values.
+template <typename TX>
+hipError_t launch_fused_row(const GemmArgs& g, const TX* X, uint8_t* o_mask, uint8_t* o_sign,
+                            float* o_alpha, int32_t* o_nnz, hipStream_t stream) {
+  int64_t P = 8;
+  while (P < g.K) P <<= 1;
+  const int64_t nch = ((g.K + 63) / 64 * 8 + 1023) / 1024;
+  const int64_t waves_needed = (g.N + 3) / 4;
+  // 16-wave blocks only for one-chunk rows: their 64-VGPR budget holds no more
+  int wb = 4;
+  if (nch <= 1 && waves_needed >= 16 * kFusedCUs) wb = 16;
+  else if (waves_needed >= 8 * kFusedCUs) wb = 8;
+#define BWTA_FR(NCH_, RUNS_, WB_) \
+  return launch_fused_row_nch<NCH_, TX, RUNS_, WB_>(g, X, o_mask, o_sign, o_alpha, o_nnz, stream)
+  if (nch <= 1) {  // P <= 8192
+    if (wb == 16) BWTA_FR(1, 1, 16);
+    if (wb == 8) BWTA_FR(1, 2, 8);
+    BWTA_FR(1, 4, 4);
+  }
+  if (nch <= 2) {  // P <= 16384
+    if (wb == 8) BWTA_FR(2, 4, 8);
+    BWTA_FR(2, 8, 4);
+  }
+  if (wb == 8) BWTA_FR(4, 8, 8);
+  BWTA_FR(4, 16, 4);
+#undef BWTA_FR
+}
+
 template <int OUT>
 hipError_t launch_gemm_pc_out(const GemmArgs& g, hipStream_t stream) {
   const int64_t row_bytes = (g.K + 63) / 64 * 8;
@@ -442,6 +735,25 @@ hipError_t launch_gemv_popcount_residual(const GemmArgs& g, hipStream_t stream) 
     case Elt::BF16: return launch_gemv_out<(int)Elt::BF16, true>(g, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// bwta_gemv_fused for one activation row (see gemv_fused_row_kernel):
+// hipErrorNotSupported when the row does not fit its fast path (M != 1, K not a
+// multiple of 8 or above kFusedMaxK, X not 16-byte aligned, ternary B).
+hipError_t launch_gemv_fused_row(const GemmArgs& g, const void* X, Elt x_dt, uint8_t* o_mask,
+                                 uint8_t* o_sign, float* o_alpha, int32_t* o_nnz,
+                                 hipStream_t stream) {
+  // Lanes read whole 16-byte words of a plane row (as gemv_popcount_kernel does,
+  // under the same condition): row_bytes % 16 keeps them inside the weight rows.
+  if (g.M != 1 || g.batch != 1 || g.b_mask || g.K % 8 != 0 || g.K > kFusedMaxK ||
+      (g.K + 63) / 64 * 8 % 16 != 0 ||
+      (x_dt != Elt::BF16 && g.K > kFusedMaxK / 2) || reinterpret_cast<uintptr_t>(X) % 16 != 0)
+    return hipErrorNotSupported;
+  return x_dt == Elt::BF16
+             ? launch_fused_row(g, static_cast<const uint16_t*>(X), o_mask, o_sign, o_alpha, o_nnz,
+                                stream)
+             : launch_fused_row(g, static_cast<const float*>(X), o_mask, o_sign, o_alpha, o_nnz,
+                                stream);
 }
 
 }  // namespace bwta

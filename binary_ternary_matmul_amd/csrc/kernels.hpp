@@ -59,15 +59,22 @@ hipError_t launch_gemv_mfma(const GemmArgs& g, hipStream_t stream);
 // Workspace bytes launch_gemv_mfma uses for this shape when one is given (0: the
 // shape runs without a cross-block split).
 size_t gemv_mfma_workspace_bytes(int64_t M, int64_t N, int64_t K);
-// The library's own per-GPU scratch array (bwta_gemv_noalloc): its size, and the
-// device address of the current device's copy (looked up, and its counter region
-// cleared on `stream`, on the first call per device).
 // Decode with the ternarization fused into the kernel: X holds M fp32 or bf16
 // rows (row stride ldx elements); g's activation planes and scales are not
 // read; o_* are optional outputs of the ternarization (NULL: not written).
 hipError_t launch_gemv_fused(const GemmArgs& g, const void* X, Elt x_dt, int64_t ldx,
                              uint8_t* o_mask, uint8_t* o_sign, float* o_alpha, int32_t* o_nnz,
                              hipStream_t stream);
+// The same for one activation row on the popcount decode kernel (gemm_popcount.hip);
+// hipErrorNotSupported, with nothing launched, outside its fast path (M != 1,
+// K % 8 != 0, K > 32768 (bf16) or 16384 (fp32), an odd number of 8-byte words
+// per plane row, X not 16-byte aligned).
+hipError_t launch_gemv_fused_row(const GemmArgs& g, const void* X, Elt x_dt, uint8_t* o_mask,
+                                 uint8_t* o_sign, float* o_alpha, int32_t* o_nnz,
+                                 hipStream_t stream);
+// The library's own per-GPU scratch array (bwta_gemv_noalloc): its size, and the
+// device address of the current device's copy (looked up, and its counter region
+// cleared on `stream`, on the first call per device).
 size_t scratch_bytes();
 hipError_t scratch_workspace(void** ptr, hipStream_t stream);
 // Two-plane residual weights, 2 <= M <= 16 (g.N outputs, 2 g.N interleaved plane rows).

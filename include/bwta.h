@@ -219,7 +219,10 @@ bwta_status bwta_gemv(const uint8_t* a_mask, const uint8_t* a_sign, const float*
  * off where the weights dominate: decode rows against large weight matrices.
  * X: M x K, row m at X + m * ldx elements, unit stride along k, BWTA_F32 or
  *    BWTA_BF16; 0 <= M <= 16 (else BWTA_ERR_UNSUPPORTED).
- * w_sign, w_alpha, Y, y_dtype, ldy: as for bwta_gemv (the FP4 decode kernel).
+ * w_sign, w_alpha, Y, y_dtype, ldy: as for bwta_gemv.  One row (M = 1, K a
+ *    multiple of 8 up to 32768 (bf16) or 16384 (fp32), row_bytes(K) a multiple
+ *    of 16, X 16-byte aligned) runs on the popcount decode kernel; everything
+ *    else on the FP4 decode kernel.  The results are the same either way.
  * a_mask, a_sign (M * row_bytes(K) bytes each, 16-byte aligned) and a_alpha,
  *    a_nnz (M entries): optional outputs, the ternarized planes and scales as
  *    bwta_ternarize_pack would write them; NULL (each pair together) = not

@@ -18,7 +18,12 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [(1, 1000, 1024), (2, 513, 8192), (4, 300, 28672), (16, 300, 28672), (3, 77, 200),
           (1, 40, 65536), (5, 100, 100), (7, 257, 1000), (4, 33, 64), (1, 17, 1),
-          (16, 1000, 28736), (9, 600, 36928)]
+          (16, 1000, 28736), (9, 600, 36928),
+          # one row: the single-row kernel's launch shapes (4-, 8- and 16-wave blocks,
+          # one, two and four 1 KiB chunks per weight row, ragged N and K) and plane
+          # rows of an odd number of 8-byte words (12344, 4104: the general kernel)
+          (1, 300, 28672), (1, 8200, 12360), (1, 2000, 16384), (1, 16500, 4168),
+          (1, 8193, 8192), (1, 8200, 12344), (1, 16500, 4104)]
 
 
 @pytest.fixture(scope="module")
