@@ -772,8 +772,8 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
 
 // Split K over S waves when that fills more SIMDs: minimise rounds(S) / S, where a
 // round is one wave on each of the 1024 SIMDs; no more waves than 256-k steps
-// (BERT's 768 x 768 products, 3 steps on 192 tiles, take S = 4: 768 waves of at
-// most one step instead of 192 waves of three).
+// (BERT's 768 x 768 product, 3 steps on 192 tiles, takes S = 2: 384 waves of one
+// or two steps instead of 192 waves of three).
 int choose_split(int64_t tiles, int64_t steps) {
   const int64_t simds = 1024;
   int best = 1;
