@@ -153,7 +153,10 @@ def test_pack_weights_columns(bw, oracle, L, C, bf16):
 GEMM_SHAPES = [(1, 1, 1), (5, 3, 64), (17, 33, 65), (128, 128, 256), (130, 260, 200),
                (40, 50, 128), (33, 70, 192), (129, 257, 320), (70, 90, 448),
                (257, 129, 1000), (128, 768, 768), (300, 130, 4096), (64, 300, 11008),
-               (200, 100, 28672 + 64)]
+               (200, 100, 28672 + 64),
+               # K split over two waves with one or two 256-k steps each, the last
+               # step holding the row end (520: a 16-byte window straddles it)
+               (150, 140, 520), (64, 1000, 330)]
 
 
 def _linear_case(oracle, M, N, K, bf16=False):
