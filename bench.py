@@ -665,6 +665,8 @@ def main():
                     help="only the attention section (unfused products and the fused call)")
     ap.add_argument("--ceilings", action="store_true",
                     help="only the measured ceilings (HBM read streams, MFMA loops)")
+    ap.add_argument("--gemv", action="store_true",
+                    help="only the decode section (GEMV shapes and the decode linear end to end)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -688,6 +690,9 @@ def main():
         return
     if args.ceilings:
         print(json.dumps({"ceilings": ceilings()}), flush=True)
+        return
+    if args.gemv:
+        print(json.dumps({"gemv": bench_gemv(bw)}), flush=True)
         return
 
     from binary_ternary_matmul_amd import inputs

@@ -10,12 +10,14 @@ from ._binding import (AttentionProbs, BinaryPlanes, BwtaError, ResidualPlanes, 
                        bwta_attention, bwta_batched_gemm, bwta_gemm, bwta_gemm_residual,
                        bwta_gemm_workspace_size, bwta_gemv, bwta_gemv_residual,
                        bwta_gemv_workspace_size, bwta_pack_weights, bwta_pack_weights_residual,
-                       bwta_gemv_fused, bwta_gemv_noalloc, bwta_ternarize_pack, lib, padded_k, row_bytes,
+                       bwta_gemv_fused, bwta_gemv_fused_workspace_size, bwta_gemv_noalloc,
+                       bwta_ternarize_pack, lib, padded_k, row_bytes, set_fused_spin_limit,
                        workspace)
 
 __all__ = ["AttentionProbs", "BinaryPlanes", "BwtaError", "ResidualPlanes", "TernaryPlanes",
            "bwta_attention", "bwta_batched_gemm", "bwta_gemm", "bwta_gemm_residual",
            "bwta_gemm_workspace_size", "bwta_gemv", "bwta_gemv_residual",
            "bwta_gemv_workspace_size", "bwta_pack_weights", "bwta_pack_weights_residual",
-           "bwta_gemv_fused", "bwta_gemv_noalloc", "bwta_ternarize_pack", "lib", "padded_k", "row_bytes",
+           "bwta_gemv_fused", "bwta_gemv_fused_workspace_size", "bwta_gemv_noalloc",
+           "bwta_ternarize_pack", "lib", "padded_k", "row_bytes", "set_fused_spin_limit",
            "workspace"]

@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
     for f in (L.bwta_gemm_workspace_size, L.bwta_gemv_workspace_size):
         f.restype = SZ
         f.argtypes = [I64, I64, I64, I32]
+    L.bwta_gemv_fused_workspace_size.restype = SZ
+    L.bwta_gemv_fused_workspace_size.argtypes = [I64, I64, I64]
+    L.bwta_set_fused_spin_limit.restype = None
+    L.bwta_set_fused_spin_limit.argtypes = [I32]
     L.bwta_batched_gemm.restype = I32
     L.bwta_batched_gemm.argtypes = [I64, P, P, P, P, I64, P, P, P, I64, I64, I64, I64, P, I32,
                                     I64, I64, I32, P]
@@ -303,7 +307,9 @@ def bwta_gemv_fused(X: torch.Tensor, w: BinaryPlanes, out_dtype: str = "f32",
                     workspace="auto"):
     """Decode linear in one launch: ternarize the rows of X [M, K] (fp32 or
     bf16, unit stride along K, M <= 16) and multiply them with w.  Returns Y, or
-    (Y, TernaryPlanes) with planes=True (the kernel's ternarization of X)."""
+    (Y, TernaryPlanes) with planes=True (the kernel's ternarization of X).
+    workspace="auto" takes the shared buffer at the size with which each row is
+    ternarized once; None runs without one (every block ternarizes the rows)."""
     if X.dtype not in (torch.float32, torch.bfloat16) or X.dim() != 2 or X.stride(1) != 1:
         raise ValueError("X must be a 2-D float32/bfloat16 tensor with unit stride along K")
     if out_dtype not in _OUT_TORCH:
@@ -327,13 +333,24 @@ def bwta_gemv_fused(X: torch.Tensor, w: BinaryPlanes, out_dtype: str = "f32",
                            torch.empty(M, dtype=torch.float32, device=dev),
                            torch.empty(M, dtype=torch.int32, device=dev), K)
     L = lib()
-    wp, wb = _workspace_arg(L.bwta_gemv_workspace_size, M, N, K, "mfma", dev, workspace)
+    wp, wb = _workspace_arg(lambda m, n, k, _a: L.bwta_gemv_fused_workspace_size(m, n, k),
+                            M, N, K, "mfma", dev, workspace)
     _check(L.bwta_gemv_fused(_ptr(X), _TORCH_DT[X.dtype], X.stride(0), _ptr(w.sign),
                              _ptr(w.alpha), M, N, K, _ptr(out), DTYPES[out_dtype], out.stride(0),
                              _ptr(tp.mask if tp else None), _ptr(tp.sign if tp else None),
                              _ptr(tp.alpha if tp else None), _ptr(tp.nnz if tp else None), wp, wb,
                              _stream()), "bwta_gemv_fused")
     return (out, tp) if planes else out
+
+
+def bwta_gemv_fused_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().bwta_gemv_fused_workspace_size(M, N, K))
+
+
+def set_fused_spin_limit(polls: int) -> None:
+    """Test hook: polls of bwta_gemv_fused's bounded wait before a block
+    ternarizes the rows itself (0: every block does; negative: the default)."""
+    lib().bwta_set_fused_spin_limit(int(polls))
 
 
 def bwta_gemv_noalloc(a: TernaryPlanes, w: BinaryPlanes, out_dtype: str = "f32",

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -16,6 +17,11 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+
+// Polls of the row flags before a block of the ternarize-once decode
+// ternarizes the rows itself (bwta_set_fused_spin_limit).
+constexpr int kDefaultFusedSpin = 1 << 16;
+std::atomic<int> g_fused_spin{kDefaultFusedSpin};
 
 bwta_status fail(bwta_status st, const char* fmt, ...) {
   va_list ap;
@@ -373,13 +379,29 @@ bwta_status bwta_gemv_fused(const void* X, bwta_dtype x_dtype, int64_t ldx, cons
     g.ws = workspace;
     g.ws_bytes = ws_bytes;
   }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
   // One row: the popcount decode kernel with the ternarization in each block.
-  const hipError_t e = bwta::launch_gemv_fused_row(g, X, elt(x_dtype), a_mask, a_sign, a_alpha,
-                                                   a_nnz, static_cast<hipStream_t>(stream));
+  hipError_t e = bwta::launch_gemv_fused_row(g, X, elt(x_dtype), a_mask, a_sign, a_alpha, a_nnz, st);
   if (e != hipErrorNotSupported) return from_hip(e, "bwta_gemv_fused launch");
-  return from_hip(bwta::launch_gemv_fused(g, X, elt(x_dtype), ldx, a_mask, a_sign, a_alpha, a_nnz,
-                                          static_cast<hipStream_t>(stream)),
+  // With room for the exchange buffers: each row ternarized once, one launch.
+  if (workspace && ws_bytes >= bwta::gemv_fused_xp_workspace_bytes(M, N, K)) {
+    e = bwta::launch_gemv_fused_xp(g, X, elt(x_dtype), ldx, a_mask, a_sign, a_alpha, a_nnz,
+                                   workspace, ws_bytes, g_fused_spin.load(), st);
+    if (e != hipErrorNotSupported) return from_hip(e, "bwta_gemv_fused launch");
+  }
+  return from_hip(bwta::launch_gemv_fused(g, X, elt(x_dtype), ldx, a_mask, a_sign, a_alpha, a_nnz, st),
                   "bwta_gemv_fused launch");
+}
+
+size_t bwta_gemv_fused_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || M > 16 || K > BWTA_MAX_K) return 0;
+  const size_t plain = bwta::gemv_mfma_workspace_bytes(M, N, K);
+  const size_t xp = bwta::gemv_fused_xp_workspace_bytes(M, N, K);
+  return xp > plain ? xp : plain;
+}
+
+void bwta_set_fused_spin_limit(int32_t polls) {
+  g_fused_spin.store(polls < 0 ? kDefaultFusedSpin : polls);
 }
 
 bwta_status bwta_gemv_noalloc(const uint8_t* a_mask, const uint8_t* a_sign, const float* a_alpha,

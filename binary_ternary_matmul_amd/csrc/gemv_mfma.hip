@@ -46,7 +46,9 @@
 //   weight stream.  S = 1: each lane applies y = (T - 2U) * (alpha_a[m] *
 //   alpha_w[n]) to its own 4 consecutive columns; S > 1: the partial tiles meet
 //   in LDS first.
+#include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -582,6 +584,10 @@ __device__ __forceinline__ void fused_ternarize(const TX* __restrict__ X, int64_
 // XT: the activations arrive as fp32 (1) or bf16 (2) rows in io.X and the block
 // ternarizes them itself (fused_ternarize) into the raw staging layout; a_mask,
 // a_sign and a_alpha are not read.
+//
+// XP: fp32 (1) or bf16 (2) rows in io.X, each ternarized once (produce_rows)
+// into the exchange buffers io.x_*, which the blocks then stage as in the plain
+// kernel (see "Ternarize-once decode"); a_mask, a_sign, a_alpha are not read.
 struct FusedIO {
   const void* X;
   int64_t ldx;
@@ -590,9 +596,238 @@ struct FusedIO {
   uint8_t* o_sign;
   float* o_alpha;
   int32_t* o_nnz;
+  int* flags;        // XP: row flags [0, 16) and the arrival counter [16]
+  int spin;          // XP: polls of the flags before a block ternarizes the rows itself
+  // XP: the exchange buffers (workspace).  Plain pointers on purpose: the
+  // kernel's restrict-qualified a_* arguments promise memory no one writes.
+  uint8_t* x_mask;
+  uint8_t* x_sign;
+  float* x_alpha;
+  int32_t* x_nnz;
+  int splits;        // XP: the cross-block K split's part count (the grid is 1-D)
 };
 
-template <int S, bool X, int OUT, bool RES = false, bool XB = false, int XT = 0>
+// ---------------------------------------------------------------------------
+// Ternarize-once decode (XP = 1 for fp32 rows, 2 for bf16; one launch, with a
+// workspace).  The exchange buffers (io.x_mask, x_sign, x_alpha, x_nnz, in the
+// workspace) receive each row's planes and scale from one block: the grid's
+// first M blocks (dispatched first) do nothing else; block m ternarizes row m
+// by the rule of bwta_ternarize_pack, stores it with device-coherent stores
+// (they reach memory, past this XCD's L2, without a cache flush; the optional
+// outputs o_* get plain copies) and raises the row's flag once they have
+// completed.  Every other block issues the first revolution of its weight ring
+// (the loads land while it waits), polls the flags with device-coherent loads
+// until all M are up, and stages the planes exactly as the plain decode kernel
+// does.  Those loads may go through L2: no block reads the exchange buffers
+// before it has seen their flags, so no L2 holds an older copy of them within
+// the launch, and launches start with the L2s invalidated.  The wait is bounded: a block
+// that has polled `spin` times ternarizes every row itself (the same values, so
+// the repeated stores change nothing) and goes on, so no block waits on another
+// without end whatever the order blocks start in.  At its end each block counts
+// itself in; the last one returns the flags and the counter to zero.
+constexpr int kXPFlags = 16;  // index of the arrival counter among the flags
+
+// The producer's block sums: the butterfly over the participating lanes by
+// xor_lane (DPP and swizzle moves, no LDS round trip per level), the same pairs
+// in the same order as block_tree, then the waves' tree through LDS.  The pair
+// form reduces the kept-value tree and the count behind one barrier.
+__device__ __forceinline__ float p_butterfly(float v, int lanes) {
+#pragma unroll
+  for (int b = 0; b < 6; ++b)
+    if ((1 << b) < lanes) v = v + xor_lane(v, 1 << b);
+  return v;
+}
+__device__ __forceinline__ int p_butterfly(int v, int lanes) {
+#pragma unroll
+  for (int b = 0; b < 6; ++b)
+    if ((1 << b) < lanes) v += xor_lane(v, 1 << b);
+  return v;
+}
+__device__ __forceinline__ float p_block_tree(float v, int NT, float* red) {
+  const int lane = __lane_id(), wid = threadIdx.x / kWave;
+  v = p_butterfly(v, NT < kWave ? NT : kWave);
+  const int nw = NT < kWave ? 1 : NT / kWave;
+  if (lane == 0 && wid < nw) red[wid] = v;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  return tree16(red, nw);
+}
+__device__ __forceinline__ void p_block_pair(float v, int c, int NT, float* red, int* ired,
+                                             float& vt, int& ct) {
+  const int lane = __lane_id(), wid = threadIdx.x / kWave;
+  const int lanes = NT < kWave ? NT : kWave;
+  v = p_butterfly(v, lanes);
+  c = p_butterfly(c, lanes);
+  const int nw = NT < kWave ? 1 : NT / kWave;
+  if (lane == 0 && wid < nw) {
+    red[wid] = v;
+    ired[wid] = c;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  vt = tree16(red, nw);
+  int s = 0;
+  for (int w = 0; w < nw; ++w) s += ired[w];
+  ct = s;
+}
+
+// REG: rows of at most 8 runs per thread keep their values in registers between
+// the passes (one round of loads); otherwise, and always with REG = false (the
+// path of a block that ternarizes the rows itself while its weight loads hold
+// registers), the values are read twice.
+template <typename TX, bool REG>
+__device__ void produce_row(const TX* __restrict__ row, int K, int row_bytes, uint8_t* lds,
+                            float* red, int* ired, uint8_t* g_mask, uint8_t* g_sign,
+                            float* g_alpha, int32_t* g_nnz, uint8_t* u_mask, uint8_t* u_sign,
+                            float* u_alpha, int32_t* u_nnz, bool vec) {
+  constexpr int NW = XRun<TX>::kWords, NG = XRun<TX>::kGroup;
+  constexpr int kRegRuns = 8;  // runs a thread holds in registers between the passes
+  int P = 1;
+  while (P < K) P <<= 1;
+  int Bp = 1;
+  while (2 * Bp <= (int)blockDim.x) Bp <<= 1;
+  const int NT = Bp < (P >= 8 ? P / 8 : 1) ? Bp : (P >= 8 ? P / 8 : 1);
+  const int V = P / NT;
+  const int runs = (V + 7) / 8;
+  const int t = threadIdx.x;
+  const bool part = t < NT;
+  const int64_t kt = (int64_t)t * V;
+  auto load = [&](int n, uint32_t (&w)[NW]) {  // run n of the thread (zeros past the row)
+    if (part && n < runs && kt + 8 * n < K)
+      x_load_run<TX>(row, kt + 8 * n, K, vec, w);
+    else
+#pragma unroll
+      for (int x = 0; x < NW; ++x) w[x] = 0u;
+  };
+  auto abs_node = [&](const uint32_t (&w)[NW]) {  // pass 1: tree(|x|) of one run
+    float a[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = __uint_as_float(x_bits(w, j, TX{}) & 0x7FFFFFFFu);
+    return lane_tree<8>(a);
+  };
+  uint32_t uthr = 0;
+  int cnt = 0;
+  auto kept_node = [&](int n, const uint32_t (&w)[NW]) {  // pass 2 of one run
+    float kept[8];
+    uint32_t mb = 0, sb = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t ux = x_bits(w, j, TX{});
+      const uint32_t ua = ux & 0x7FFFFFFFu;
+      const uint32_t keep = (uthr - ua) >> 31;  // |x| > thr (non-negative bit patterns)
+      kept[j] = __uint_as_float(ua & (0u - keep));
+      mb |= keep << j;
+      sb |= (keep & (ux >> 31)) << j;
+    }
+    cnt += __builtin_popcount(mb);
+    const int64_t k0 = kt + 8 * n;
+    if (part && k0 < (int64_t)row_bytes * 8) {
+      lds[k0 >> 3] = (uint8_t)mb;
+      lds[row_bytes + (k0 >> 3)] = (uint8_t)sb;
+    }
+    return lane_tree<8>(kept);
+  };
+  // the row's planes in LDS (mask, then sign), cleared: bytes no run covers stay 0
+  uint32_t* lw = reinterpret_cast<uint32_t*>(lds);
+  for (int i = t; i < row_bytes / 2; i += blockDim.x) lw[i] = 0u;
+  float st[kXStack];
+#pragma unroll
+  for (int l = 0; l < kXStack; ++l) st[l] = 0.0f;
+  float ktot;
+  if (REG && runs <= kRegRuns) {
+    // one round of loads; the values stay in registers for pass 2
+    uint32_t w[kRegRuns][NW];
+#pragma unroll
+    for (int n = 0; n < kRegRuns; ++n) load(n, w[n]);
+#pragma unroll
+    for (int n = 0; n < kRegRuns; ++n)
+      if (n < runs) stack_push(st, n, abs_node(w[n]));
+    // (its barrier also orders the clearing before the plane bytes below)
+    const float total = p_block_tree(part ? stack_root(st, runs) : 0.0f, NT, red);
+    uthr = __float_as_uint(0.5f * (total / (float)K));
+#pragma unroll
+    for (int l = 0; l < kXStack; ++l) st[l] = 0.0f;
+#pragma unroll
+    for (int n = 0; n < kRegRuns; ++n)
+      if (n < runs) stack_push(st, n, kept_node(n, w[n]));
+  } else {
+    // long runs: the values read twice, NG runs at a time
+    for (int g0 = 0; g0 < runs; g0 += NG) {
+      uint32_t w[NG][NW];
+#pragma unroll
+      for (int i = 0; i < NG; ++i) load(g0 + i, w[i]);
+#pragma unroll
+      for (int i = 0; i < NG; ++i)
+        if (g0 + i < runs) stack_push(st, g0 + i, abs_node(w[i]));
+    }
+    const float total = p_block_tree(part ? stack_root(st, runs) : 0.0f, NT, red);
+    uthr = __float_as_uint(0.5f * (total / (float)K));
+#pragma unroll
+    for (int l = 0; l < kXStack; ++l) st[l] = 0.0f;
+    for (int g0 = 0; g0 < runs; g0 += NG) {
+      uint32_t w[NG][NW];
+#pragma unroll
+      for (int i = 0; i < NG; ++i) load(g0 + i, w[i]);
+#pragma unroll
+      for (int i = 0; i < NG; ++i)
+        if (g0 + i < runs) stack_push(st, g0 + i, kept_node(g0 + i, w[i]));
+    }
+  }
+  // (its barrier orders the plane bytes before the word reads below)
+  int ctot;
+  p_block_pair(part ? stack_root(st, runs) : 0.0f, part ? cnt : 0, NT, red + 8, ired, ktot, ctot);
+  const float alpha = ctot ? ktot / (float)ctot : 0.0f;
+  const int words = row_bytes / 4;
+  for (int i = t; i < words; i += blockDim.x) {
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(g_mask) + i, lw[i], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(g_sign) + i, lw[words + i], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (u_mask)
+    for (int i = t; i < words; i += blockDim.x) {
+      reinterpret_cast<uint32_t*>(u_mask)[i] = lw[i];
+      reinterpret_cast<uint32_t*>(u_sign)[i] = lw[words + i];
+    }
+  if (t == 0) {
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(g_alpha), __float_as_uint(alpha),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(g_nnz, ctot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (u_alpha) {
+      *u_alpha = alpha;
+      *u_nnz = ctot;
+    }
+  }
+  // every store of the block has completed before the barrier, and the LDS
+  // planes are read before anything overwrites them
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait0());
+  lds_barrier();
+}
+
+// Rows m = first, first + step, ... < M of X into the exchange buffers, each
+// followed by its flag (after the row's stores have completed).  The flag
+// stores complete before the block's arrival count (xp_arrive).
+template <typename TX, bool REG>
+__device__ void produce_rows(const FusedIO& io, int M, int row_bytes, int first, int step,
+                             uint8_t* lds, float* red, int* ired, uint8_t* x_mask,
+                             uint8_t* x_sign, float* x_alpha, int32_t* x_nnz) {
+  const TX* X = static_cast<const TX*>(io.X);
+  const bool vec = (reinterpret_cast<uintptr_t>(X) % 16 == 0) &&
+                   ((io.ldx * (int64_t)sizeof(TX)) % 16 == 0) && (io.K % 8 == 0);
+  for (int m = first; m < M; m += step) {
+    const int64_t ro = (int64_t)m * row_bytes;
+    produce_row<TX, REG>(X + (int64_t)m * io.ldx, io.K, row_bytes, lds, red, ired, x_mask + ro,
+                         x_sign + ro, x_alpha + m, x_nnz + m, io.o_mask ? io.o_mask + ro : nullptr,
+                         io.o_mask ? io.o_sign + ro : nullptr, io.o_alpha ? io.o_alpha + m : nullptr,
+                         io.o_alpha ? io.o_nnz + m : nullptr, vec);
+    if (threadIdx.x == 0)  // (completed before the block counts itself in)
+      __hip_atomic_store(io.flags + m, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int S, bool X, int OUT, bool RES = false, bool XB = false, int XT = 0, int XP = 0>
 __global__ void __launch_bounds__(kMaxW * kWave)
 gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__ a_sign,
                  const float* __restrict__ a_alpha, int M, const uint8_t* __restrict__ w_sign,
@@ -601,8 +836,10 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
                  int* __restrict__ ws_part, FusedIO io) {
   static_assert(!XB || (S == 1 && !RES), "the cross-block split runs unsplit one-plane waves");
   static_assert(XT == 0 || (!X && !RES), "fused ternarization stages raw one-plane operands");
+  static_assert(XP == 0 || (XT == 0 && !RES), "ternarize-once decode stages one-plane operands");
   __shared__ float s_alpha[16], s_red[16 * 8], s_red2[16 * 8];
-  __shared__ int s_nnz[16], s_ired[16 * 8];
+  __shared__ int s_nnz[16], s_ired[16 * 8], s_xp;
+  typedef typename std::conditional<XP == 1, float, uint16_t>::type XPT;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int W = blockDim.x / kWave;
   const int R = W / S;  // row groups per block
@@ -614,7 +851,37 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   static_assert(!RES || OUT != (int)Elt::I32, "two-plane products are scaled");
   constexpr int PF = RES ? kPF / 2 : kPF;  // chunks per batch and plane
   constexpr int RING = PF * kNB;
-  const int64_t ot = (int64_t)blockIdx.x * R + rg;  // output tile
+  // XP: a 1-D grid whose first M blocks only ternarize; block M + c is the
+  // consumer (c % cblocks, c / cblocks) of the plain 2-D grid.
+  const int nblk = (int)(gridDim.x * gridDim.y);
+  const int nsplit = XB ? (XP != 0 ? io.splits : (int)gridDim.y) : 1;
+  const int cblocks = XP != 0 ? (nblk - M) / nsplit : (int)gridDim.x;
+  const int c_lin = XP != 0 ? (int)blockIdx.x - M : 0;
+  const int bx = XP != 0 ? c_lin % cblocks : (int)blockIdx.x;
+  const int by = XP != 0 ? c_lin / cblocks : (int)blockIdx.y;
+  // The block is past its wait (and its flag stores have completed): count it
+  // in; the last one clears the flags.
+  auto xp_arrive = [&]() {
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_wait0());
+      const int old = __hip_atomic_fetch_add(io.flags + kXPFlags, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      if (old == nblk - 1) {
+        for (int m = 0; m < M; ++m)
+          __hip_atomic_store(io.flags + m, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(io.flags + kXPFlags, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  };
+  if constexpr (XP != 0) {
+    if ((int)blockIdx.x < M) {  // 0. a producing block: its row, then nothing else
+      produce_rows<XPT, true>(io, M, row_bytes, (int)blockIdx.x, M, smem, s_red, s_ired, io.x_mask,
+                              io.x_sign, io.x_alpha, io.x_nnz);
+      xp_arrive();
+      return;
+    }
+  }
+  const int64_t ot = (int64_t)bx * R + rg;  // output tile
   const int64_t n0 = ot * 16;
   const int64_t p1 = RES ? 64 * (ot >> 1) + 16 * (ot & 1) : n0;  // its (first) plane rows
   const int64_t rows_left = N - n0;
@@ -622,21 +889,23 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   // The block's chunk range [kc0, kc0 + chunks) (all of the row unless XB); LDS
   // holds it at local chunk indices 0 .. chunks - 1.
   const int all_chunks = (row_bytes + 63) / 64;
-  const int ky = XB ? (int)blockIdx.y : 0;
-  const int nsplit = XB ? (int)gridDim.y : 1;
+  const int ky = XB ? by : 0;
   const int kc0 = XB ? all_chunks * ky / nsplit : 0;
   const int chunks = XB ? all_chunks * (ky + 1) / nsplit - kc0 : all_chunks;
   const int c0 = kc0 + chunks * ks / S;
   const int c1 = kc0 + chunks * (ks + 1) / S;
   const LdsLayout L = lds_layout(X, chunks, M, S, R, RES ? 2 : 1);
   int* tsum = reinterpret_cast<int*>(smem + L.t_off);
+  // the planes the block stages: the exchange buffers (XP) or the arguments
+  const uint8_t* const st_mask = XP != 0 ? io.x_mask : a_mask;
+  const uint8_t* const st_sign = XP != 0 ? io.x_sign : a_sign;
 
   // 1. Epilogue scales.  Items: S = 1, the lanes of the own wave; S > 1, item
   //    p = threadIdx.x (row group p / 64, lane p % 64) when p < R * 64.
   constexpr int ES = OUT == (int)Elt::BF16 ? 2 : 4;
   const int p_item = S == 1 ? lane : (int)threadIdx.x;
   const bool item_ok = S == 1 || p_item < R * kWave;
-  const int64_t nb_item = S == 1 ? n0 : ((int64_t)blockIdx.x * R + p_item / kWave) * 16;
+  const int64_t nb_item = S == 1 ? n0 : ((int64_t)bx * R + p_item / kWave) * 16;
   const int l_item = p_item % kWave;
   v4f ab = v4f{0.0f, 0.0f, 0.0f, 0.0f}, ab2 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   float aa = 0.0f;
@@ -651,7 +920,7 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     if constexpr (RES)
       ab2 = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
                                         ars, (int)(n < N ? (uint32_t)((pn + 32) * 4) : kOOB), 0, 0));
-    if constexpr (XT == 0) {
+    if constexpr (XT == 0 && XP == 0) {
       const __amdgpu_buffer_rsrc_t aars = checked_rsrc(a_alpha, (uint32_t)M * 4u);
       aa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                          aars, (int)((l_item & 15) * 4), 0, 0));
@@ -676,20 +945,23 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     c = q - m * chunks;
   };
   const int nsu = XT ? 0 : (units + (int)blockDim.x - 1) / (int)blockDim.x;  // rounds, uniform
-  const __amdgpu_buffer_rsrc_t mrs = checked_rsrc(a_mask, (uint32_t)M * (uint32_t)row_bytes);
-  const __amdgpu_buffer_rsrc_t srs = checked_rsrc(a_sign, (uint32_t)M * (uint32_t)row_bytes);
+  const __amdgpu_buffer_rsrc_t mrs = checked_rsrc(st_mask, (uint32_t)M * (uint32_t)row_bytes);
+  const __amdgpu_buffer_rsrc_t srs = checked_rsrc(st_sign, (uint32_t)M * (uint32_t)row_bytes);
   v4u sm[kMaxSU], ss[kMaxSU];
+  auto stage_loads = [&]() {
 #pragma unroll
-  for (int k = 0; k < kMaxSU; ++k) {
-    if (k < nsu) {
-      const int u = (int)threadIdx.x + k * (int)blockDim.x;
-      int m, c, gg;
-      unit_pos(u, m, c, gg);
-      const uint32_t off = u < units ? (uint32_t)(m * row_bytes + 64 * (kc0 + c) + 16 * gg) : kOOB;
-      sm[k] = __builtin_amdgcn_raw_buffer_load_b128(mrs, (int)off, 0, 0);
-      ss[k] = __builtin_amdgcn_raw_buffer_load_b128(srs, (int)off, 0, 0);
+    for (int k = 0; k < kMaxSU; ++k) {
+      if (k < nsu) {
+        const int u = (int)threadIdx.x + k * (int)blockDim.x;
+        int m, c, gg;
+        unit_pos(u, m, c, gg);
+        const uint32_t off = u < units ? (uint32_t)(m * row_bytes + 64 * (kc0 + c) + 16 * gg) : kOOB;
+        sm[k] = __builtin_amdgcn_raw_buffer_load_b128(mrs, (int)off, 0, 0);
+        ss[k] = __builtin_amdgcn_raw_buffer_load_b128(srs, (int)off, 0, 0);
+      }
     }
-  }
+  };
+  if constexpr (XP == 0) stage_loads();
 
   // 3. Weight ring: slot (b, i) holds chunk base + b * kPF + i of the current
   //    revolution.  Batch 0 goes out now, the others once the activations are
@@ -711,7 +983,37 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     }
   };
   issue(0, c0);
+  if constexpr (XP != 0) {
+#pragma unroll
+    for (int b = 1; b < kNB; ++b) issue(b, c0 + b * PF);
+  }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (XP != 0) {
+    // Wait (bounded) for every row's flag under the first revolution of the
+    // weight ring.
+    if (wid == 0) {
+      int ok = 0;
+      for (int it = 0;; ++it) {
+        const int v =
+            lane < M ? __hip_atomic_load(io.flags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1;
+        ok = __all(v != 0);
+        if (ok || it >= io.spin) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (lane == 0) s_xp = ok;
+    }
+    lds_barrier();
+    if (!s_xp)  // not all rows ready in time: ternarize them here as well
+      produce_rows<XPT, false>(io, M, row_bytes, 0, 1, smem, s_red, s_ired, io.x_mask, io.x_sign,
+                               io.x_alpha, io.x_nnz);
+    // no load of the exchange buffers may move above the wait
+    __asm__ volatile("" ::: "memory");
+    if constexpr (OUT != (int)Elt::I32) {
+      const int m = l_item & 15;
+      aa = m < M ? io.x_alpha[m] : 0.0f;
+    }
+    stage_loads();
+  }
 
   // 4. Staging stores (they wait for the staging loads only) and row sums T,
   //    accumulated per wave in its own 16 LDS counters (cleared by the wave
@@ -794,8 +1096,10 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
     if (threadIdx.x < 2)
       *reinterpret_cast<v4u*>(smem + L.zero_off + 16 * threadIdx.x) = v4u{0u, 0u, 0u, 0u};
   }
+  if constexpr (XP == 0) {
 #pragma unroll
-  for (int b = 1; b < kNB; ++b) issue(b, c0 + b * PF);
+    for (int b = 1; b < kNB; ++b) issue(b, c0 + b * PF);
+  }
   __builtin_amdgcn_sched_barrier(0);
   lds_barrier();
   if constexpr (XT != 0) aa = s_alpha[l_item & 15];  // 0 for rows m >= M (never stored)
@@ -984,6 +1288,7 @@ gemv_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
       store(l_item, sum, sum2, nb_item);
     }
   }
+  if constexpr (XP != 0) xp_arrive();
 }
 
 // Launch geometry for one group of mg activation rows.
@@ -1032,7 +1337,8 @@ struct Split {
 };
 
 constexpr int64_t kMaxSplitTiles = 4096;  // P x tiles: at most 4 MiB of partials
-constexpr size_t kCtrBytes = 8192;        // counters of up to 2048 tiles (P >= 2)
+constexpr size_t kCtrBytes = 8192;        // the region that is zero between calls
+constexpr size_t kFlagBytes = 256;        // its last bytes: the fused decode's row flags
 
 Split split_plan(int64_t M, int64_t N, int64_t row_bytes) {
   Split sp;
@@ -1045,7 +1351,7 @@ Split split_plan(int64_t M, int64_t N, int64_t row_bytes) {
   const int64_t chunks = (row_bytes + 63) / 64;
   int P = q1.S;
   while (P > 1 && tiles * P > kMaxSplitTiles) P /= 2;
-  if (P < 2 || tiles * 4 > (int64_t)kCtrBytes) return sp;
+  if (P < 2 || tiles * 4 > (int64_t)(kCtrBytes - kFlagBytes)) return sp;
   const int64_t cb = (chunks + P - 1) / P;  // the largest range
   int64_t R = (tiles * P + 255) / 256;
   if (R < 1) R = 1;
@@ -1063,11 +1369,11 @@ Split split_plan(int64_t M, int64_t N, int64_t row_bytes) {
 }
 
 // io: the fused ternarization's rows (XT != 0; offset here to the group's rows).
-template <int S, bool X, int OUT, bool RES = false, bool XB = false, int XT = 0>
+template <int S, bool X, int OUT, bool RES = false, bool XB = false, int XT = 0, int XP = 0>
 hipError_t launch_s(const GemmArgs& g, const Geometry& q, int64_t m0, int64_t mg,
                     int64_t row_bytes, hipStream_t stream, int splits = 1, int* ctr = nullptr,
                     int* part = nullptr, FusedIO io = FusedIO{}) {
-  auto kfn = gemv_mfma_kernel<S, X, OUT, RES, XB, XT>;
+  auto kfn = gemv_mfma_kernel<S, X, OUT, RES, XB, XT, XP>;
   hipError_t e = hipFuncSetAttribute((const void*)kfn,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)q.lds);
   if (e != hipSuccess) return e;
@@ -1081,7 +1387,10 @@ hipError_t launch_s(const GemmArgs& g, const Geometry& q, int64_t m0, int64_t mg
   }
   const uint8_t* am = g.a_mask ? g.a_mask + m0 * row_bytes : nullptr;
   const uint8_t* as = g.a_sign ? g.a_sign + m0 * row_bytes : nullptr;
-  hipLaunchKernelGGL(kfn, dim3((unsigned)q.blocks, (unsigned)splits),
+  if constexpr (XP != 0) io.splits = splits;
+  const dim3 grid = XP != 0 ? dim3((unsigned)(mg + q.blocks * splits))
+                            : dim3((unsigned)q.blocks, (unsigned)splits);
+  hipLaunchKernelGGL(kfn, grid,
                      dim3((unsigned)(q.S * q.R * kWave)), q.lds, stream, am, as,
                      g.a_alpha ? g.a_alpha + m0 : nullptr, (int)mg, g.b_sign, g.b_alpha, g.N,
                      (int)row_bytes, static_cast<char*>(g.Y) + m0 * g.ldy * ES, g.ldy, ctr, part,
@@ -1136,6 +1445,51 @@ hipError_t launch_fused(const GemmArgs& g, const FusedIO& io, hipStream_t stream
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// Ternarize-once decode (XP = 1 fp32, 2 bf16 rows): one launch over all M rows
+// on the plain decode plan (the cross-block split where g.ws has one), with LDS
+// for a producing block's row planes at least.  hipErrorNotSupported when the
+// rows' staging does not fit one launch.  io.x_* are the exchange buffers.
+template <int OUT, int XP>
+hipError_t launch_xp(const GemmArgs& g, const FusedIO& io, hipStream_t stream) {
+  if (g.N >= (int64_t)1 << 29) return hipErrorInvalidValue;  // 32-bit offsets
+  const int64_t row_bytes = (g.K + 63) / 64 * 8;
+  const size_t prod = (size_t)(2 * row_bytes);
+  const Split sp = g.ws ? split_plan(g.M, g.N, row_bytes) : Split{};
+  if (sp.use) {
+    if (g.ws_bytes < sp.ws_bytes) return hipErrorInvalidValue;
+    Geometry q;
+    q.S = 1;
+    q.R = sp.R;
+    q.X = sp.X;
+    q.blocks = sp.blocks;
+    q.lds = std::max(sp.lds, prod);
+    q.fits = q.lds <= kMaxLds;
+    if (!q.fits) return hipErrorNotSupported;
+    int* ctr = static_cast<int*>(g.ws);
+    int* part = reinterpret_cast<int*>(static_cast<char*>(g.ws) + sp.ctr_bytes);
+    return sp.X ? launch_s<1, true, OUT, false, true, 0, XP>(g, q, 0, g.M, row_bytes, stream,
+                                                             sp.P, ctr, part, io)
+                : launch_s<1, false, OUT, false, true, 0, XP>(g, q, 0, g.M, row_bytes, stream,
+                                                              sp.P, ctr, part, io);
+  }
+  Geometry q = geometry(g.N, row_bytes, g.M);
+  if (!q.fits) return hipErrorNotSupported;
+  q.lds = std::max(q.lds, prod);
+  if (q.lds > kMaxLds) return hipErrorNotSupported;
+#define BWTA_XP_S(SS)                                                                          \
+  return q.X ? launch_s<SS, true, OUT, false, false, 0, XP>(g, q, 0, g.M, row_bytes, stream, 1,  \
+                                                           nullptr, nullptr, io)               \
+             : launch_s<SS, false, OUT, false, false, 0, XP>(g, q, 0, g.M, row_bytes, stream, 1, \
+                                                            nullptr, nullptr, io)
+  switch (q.S) {
+    case 1: BWTA_XP_S(1);
+    case 2: BWTA_XP_S(2);
+    case 4: BWTA_XP_S(4);
+    default: BWTA_XP_S(8);
+  }
+#undef BWTA_XP_S
 }
 
 template <bool X, int OUT, bool RES = false>
@@ -1277,6 +1631,65 @@ hipError_t launch_gemv_fused(const GemmArgs& g, const void* X, Elt x_dt, int64_t
       return bf ? launch_fused<(int)Elt::BF16, 2>(g, io, stream) : launch_fused<(int)Elt::BF16, 1>(g, io, stream);
     case Elt::I32:
       return bf ? launch_fused<(int)Elt::I32, 2>(g, io, stream) : launch_fused<(int)Elt::I32, 1>(g, io, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Workspace of the ternarize-once decode: the decode kernel's own region (split
+// counters and partial tiles; none for shapes that never split), whose counter
+// region (zero between calls, the same for every shape) ends with the row
+// flags, then the exchange planes and scales.  The flags sit at the same offset
+// for every shape, inside a region no call leaves non-zero, so calls of any
+// shapes can share one workspace.
+struct XPLayout {
+  size_t split, flags, mask, sign, alpha, nnz, total;
+};
+
+XPLayout xp_layout(int64_t M, int64_t N, int64_t K) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const size_t plane = (size_t)M * (size_t)((K + 63) / 64 * 8);
+  XPLayout l;
+  l.split = gemv_mfma_workspace_bytes(M, N, K);
+  l.flags = kCtrBytes - kFlagBytes;
+  l.mask = up(l.split > kCtrBytes ? l.split : kCtrBytes);
+  l.sign = l.mask + up(plane);
+  l.alpha = l.sign + up(plane);
+  l.nnz = l.alpha + up((size_t)M * 4);
+  l.total = l.nnz + up((size_t)M * 4);
+  return l;
+}
+
+size_t gemv_fused_xp_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || M > 16) return 0;
+  return xp_layout(M, N, K).total;
+}
+
+hipError_t launch_gemv_fused_xp(const GemmArgs& g, const void* X, Elt x_dt, int64_t ldx,
+                                uint8_t* o_mask, uint8_t* o_sign, float* o_alpha,
+                                int32_t* o_nnz, void* ws, size_t ws_bytes, int spin,
+                                hipStream_t stream) {
+  if (g.M < 1 || g.M > 16 || !ws) return hipErrorNotSupported;
+  const XPLayout l = xp_layout(g.M, g.N, g.K);
+  if (ws_bytes < l.total || reinterpret_cast<uintptr_t>(ws) % 256 != 0) return hipErrorNotSupported;
+  char* base = static_cast<char*>(ws);
+  uint8_t* ex_mask = reinterpret_cast<uint8_t*>(base + l.mask);
+  uint8_t* ex_sign = reinterpret_cast<uint8_t*>(base + l.sign);
+  float* ex_alpha = reinterpret_cast<float*>(base + l.alpha);
+  int32_t* ex_nnz = reinterpret_cast<int32_t*>(base + l.nnz);
+  GemmArgs g2 = g;
+  g2.ws = l.split ? ws : nullptr;
+  g2.ws_bytes = l.split;
+  const FusedIO io{X, ldx, (int)g.K, o_mask, o_sign, o_alpha, o_nnz,
+                   reinterpret_cast<int*>(base + l.flags), spin < 0 ? 0 : spin,
+                   ex_mask, ex_sign, ex_alpha, ex_nnz, 1};
+  const bool bf = x_dt == Elt::BF16;
+  switch (g.y_dt) {
+    case Elt::F32:
+      return bf ? launch_xp<(int)Elt::F32, 2>(g2, io, stream) : launch_xp<(int)Elt::F32, 1>(g2, io, stream);
+    case Elt::BF16:
+      return bf ? launch_xp<(int)Elt::BF16, 2>(g2, io, stream) : launch_xp<(int)Elt::BF16, 1>(g2, io, stream);
+    case Elt::I32:
+      return bf ? launch_xp<(int)Elt::I32, 2>(g2, io, stream) : launch_xp<(int)Elt::I32, 1>(g2, io, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -65,6 +65,18 @@ size_t gemv_mfma_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv_fused(const GemmArgs& g, const void* X, Elt x_dt, int64_t ldx,
                              uint8_t* o_mask, uint8_t* o_sign, float* o_alpha, int32_t* o_nnz,
                              hipStream_t stream);
+// The same with each row ternarized once, by one block, into exchange buffers
+// (o_* when given, else workspace memory) that every block then stages; one
+// launch.  ws: at least gemv_fused_xp_workspace_bytes, 256-byte aligned, its
+// flag region zero before the first call (each call leaves it zero).  spin:
+// polls of the row flags before a block ternarizes the rows itself.
+// hipErrorNotSupported, with nothing launched, when the workspace is missing or
+// short or the rows' staging does not fit one launch.
+size_t gemv_fused_xp_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemv_fused_xp(const GemmArgs& g, const void* X, Elt x_dt, int64_t ldx,
+                                uint8_t* o_mask, uint8_t* o_sign, float* o_alpha,
+                                int32_t* o_nnz, void* ws, size_t ws_bytes, int spin,
+                                hipStream_t stream);
 // The same for one activation row on the popcount decode kernel (gemm_popcount.hip);
 // hipErrorNotSupported, with nothing launched, outside its fast path (M != 1,
 // K % 8 != 0, K > 32768 (bf16) or 16384 (fp32), an odd number of 8-byte words

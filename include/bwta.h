@@ -214,9 +214,16 @@ bwta_status bwta_gemv(const uint8_t* a_mask, const uint8_t* a_sign, const float*
  * online and a bit-packed binary/ternary MatMul; the replies quoted on the page
  * name decode as a workload): ternarize the M rows of X by the rule of
  * bwta_ternarize_pack and multiply them with the binary weights as bwta_gemv
- * does, without the activation planes going through memory.  Every thread
- * block ternarizes the rows itself (M * K values per block), so the call pays
- * off where the weights dominate: decode rows against large weight matrices.
+ * does.  How the rows are ternarized depends on the workspace:
+ *   at least bwta_gemv_fused_workspace_size(M, N, K) bytes: each row once, by
+ *     one thread block, into exchange buffers (a_mask ... a_nnz when given,
+ *     else workspace memory) that the other blocks wait for (a bounded wait:
+ *     a block that waits too long ternarizes the rows itself) and then stage
+ *     as bwta_gemv does;
+ *   otherwise (NULL or smaller): every thread block ternarizes the rows
+ *     itself (M * K values per block) and the planes never go through memory.
+ * One row that fits the popcount decode kernel (below) always takes the
+ * second form, which is the faster one there.
  * X: M x K, row m at X + m * ldx elements, unit stride along k, BWTA_F32 or
  *    BWTA_BF16; 0 <= M <= 16 (else BWTA_ERR_UNSUPPORTED).
  * w_sign, w_alpha, Y, y_dtype, ldy: as for bwta_gemv.  One row (M = 1, K a
@@ -227,13 +234,26 @@ bwta_status bwta_gemv(const uint8_t* a_mask, const uint8_t* a_sign, const float*
  *    a_nnz (M entries): optional outputs, the ternarized planes and scales as
  *    bwta_ternarize_pack would write them; NULL (each pair together) = not
  *    written.
- * workspace, ws_bytes: as for bwta_gemv, sized by
- *    bwta_gemv_workspace_size(M, N, K, BWTA_ALGO_MFMA). */
+ * workspace, ws_bytes: as for bwta_gemv (NULL allowed; if given, at least
+ *    bwta_gemv_workspace_size(M, N, K, BWTA_ALGO_MFMA) bytes, zero-filled once
+ *    before its first use; every call leaves it as the next call needs it). */
 bwta_status bwta_gemv_fused(const void* X, bwta_dtype x_dtype, int64_t ldx, const uint8_t* w_sign,
                             const float* w_alpha, int64_t M, int64_t N, int64_t K, void* Y,
                             bwta_dtype y_dtype, int64_t ldy, uint8_t* a_mask, uint8_t* a_sign,
                             float* a_alpha, int32_t* a_nnz, void* workspace, size_t ws_bytes,
                             void* stream);
+
+/* Workspace bytes with which bwta_gemv_fused ternarizes each row once: the
+ * decode kernel's own workspace, 256 bytes of row flags and room for the
+ * exchange planes and scales.  0 for M < 1, M > 16, N < 1 or K out of range. */
+size_t bwta_gemv_fused_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* Test hook of bwta_gemv_fused's bounded wait: the number of polls of the row
+ * flags after which a thread block ternarizes the rows itself (default 65536;
+ * a negative value restores it).  0 makes every block ternarize every row, the
+ * path a block takes if the blocks that own the rows have not run in time.
+ * The result is the same either way.  Affects calls made after it returns. */
+void bwta_set_fused_spin_limit(int32_t polls);
 
 /* bwta_gemv for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same

@@ -135,6 +135,29 @@ def test_workspace_size_query(L):
     assert gm(16, 8192, 28672, MFMA) == 0 and gm(64, 8192, 28672, AUTO) == 0
 
 
+def test_fused_workspace_size_query(L):
+    """The fused decode's workspace: the decode kernel's own bytes at least, the
+    8 KiB counter region always (its last 256 bytes hold the row flags), plus the
+    exchange planes (2 M row_bytes) and scales; 0 outside 1 <= M <= 16."""
+    L.bwta_gemv_fused_workspace_size.restype = ctypes.c_size_t
+    L.bwta_gemv_fused_workspace_size.argtypes = [ctypes.c_int64] * 3
+    L.bwta_gemv_workspace_size.restype = ctypes.c_size_t
+    L.bwta_gemv_workspace_size.argtypes = [ctypes.c_int64] * 3 + [ctypes.c_int32]
+    fz, gv = L.bwta_gemv_fused_workspace_size, L.bwta_gemv_workspace_size
+    for M, N, K in [(16, 8192, 28672), (4, 28672, 8192), (1, 100, 1), (9, 600, 36928)]:
+        rb = (K + 63) // 64 * 8
+        need = fz(M, N, K)
+        assert need % 256 == 0
+        assert need >= max(gv(M, N, K, 1), 8192) + 2 * M * rb + 8 * M
+        assert need <= max(gv(M, N, K, 1), 8192) + 2 * (M * rb + 255) + 512
+    assert fz(0, 8192, 28672) == 0 and fz(17, 8192, 28672) == 0 and fz(4, 0, 8192) == 0
+    assert fz(4, 8192, 0) == 0
+    L.bwta_set_fused_spin_limit.restype = None
+    L.bwta_set_fused_spin_limit.argtypes = [ctypes.c_int32]
+    L.bwta_set_fused_spin_limit(0)
+    L.bwta_set_fused_spin_limit(-1)  # back to the default
+
+
 @pytest.mark.parametrize("fn", ["bwta_gemm", "bwta_gemv"])
 def test_workspace_validation(L, fn):
     shape = dict(M=16, N=8192, K=28672, ldy=8192)

@@ -81,3 +81,40 @@ def test_gemv_fused_zero_rows(bw, oracle):
     x[1] = 0
     x[3] = 0x8000  # -0.0 in every column
     _check(bw, oracle, x, _w(10, N, K), to_dev(x), "auto")
+
+
+# With the workspace ("auto" above) each row is ternarized once by one block and
+# the other blocks wait for its flag.  The wait is bounded: a block that has polled
+# the flags `spin` times ternarizes every row itself.  Spin 0 forces that path on
+# every block (the kernel still ends normally; the rows are written several times
+# with the same values).
+@pytest.mark.parametrize("M,N,K", [(2, 513, 8192), (16, 300, 28672), (5, 100, 100),
+                                   (9, 600, 36928), (1, 8200, 12344), (3, 77, 200)])
+def test_gemv_fused_every_block_ternarizes(bw, oracle, M, N, K):
+    x = _x(M * 7 + N, M, K, True)
+    w = _w(N * 3 + K, N, K)
+    bw.set_fused_spin_limit(0)
+    try:
+        _check(bw, oracle, x, w, to_dev(x), "auto")
+    finally:
+        bw.set_fused_spin_limit(-1)
+
+
+def test_gemv_fused_calls_in_a_row(bw, oracle):
+    """Calls of different M and K on one shared workspace: every call must find
+    the row flags and the arrival counter zero, and leave them so."""
+    import torch
+    shapes = [(16, 1000, 8192), (4, 1000, 8192), (16, 520, 28672), (2, 64, 520), (16, 1000, 8192),
+              (7, 3000, 4096)]
+    for i, (M, N, K) in enumerate(shapes):
+        x = _x(1000 + i, M, K, i % 2 == 0)
+        w = _w(2000 + i, N, K)
+        wp = bw.bwta_pack_weights(to_dev(w))
+        t, alpha, nnz = oracle.ternarize(x)
+        s, w_alpha = oracle.binarize(w)
+        y_ref = oracle.scale(oracle.matmul_i32(t, s, threads=8), alpha, w_alpha)
+        y = to_host(bw.bwta_gemv_fused(to_dev(x), wp, "f32", workspace="auto"))
+        assert (y.view(np.uint32) == y_ref.view(np.uint32)).all(), f"call {i} {M}x{N}x{K} differs"
+    # the split counters and the row flags (the first 8 KiB) are zero again
+    ws = bw.workspace(torch.device("cuda", torch.cuda.current_device()), 0)
+    assert int(ws[:8192].count_nonzero()) == 0, "counters or flags left non-zero"
