@@ -614,8 +614,8 @@ def calibrate_copy(nbytes=256 << 20, reps=3):
 
 def profile_gemv(bw, copies=4):
     """A few cold launches of each decode shape, of gate/up stacked into one
-    [57344, 8192] weight, and (M = 1) of the fused decode call (for profiler
-    counters)."""
+    [57344, 8192] weight, and of the fused decode call (bf16 rows in, the
+    shared workspace) for profiler counters."""
     import torch
     from binary_ternary_matmul_amd import inputs
     up = None
@@ -640,12 +640,12 @@ def profile_gemv(bw, copies=4):
                     bw.bwta_gemv(a, wi, "f32", "auto", y2)
                 torch.cuda.synchronize()
                 del fs
-            if M == 1:  # the decode linear in one launch, bf16 row in
-                X = dev(lin.x())
-                torch.cuda.synchronize()
-                for wi in ws:
-                    bw.bwta_gemv_fused(X, wi, "f32", y)
-                torch.cuda.synchronize()
+            X = dev(lin.x())  # the decode linear in one launch, bf16 rows in
+            bw.bwta_gemv_fused(X, ws[0], "f32", y)  # (sizes the shared workspace)
+            torch.cuda.synchronize()
+            for wi in ws:
+                bw.bwta_gemv_fused(X, wi, "f32", y)
+            torch.cuda.synchronize()
             del ws, w
     print(json.dumps({"profile_gemv": "done", "copies": copies}), flush=True)
 
