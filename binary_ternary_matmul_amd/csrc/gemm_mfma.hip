@@ -45,6 +45,9 @@
 // * Tiles go to the XCDs in bands of 8 tile rows, so each XCD's L2 holds a
 //   compact set of A and B panels; complete tiles store their output rows
 //   through LDS, whole rows per 16-byte store.
+#include <algorithm>
+#include <vector>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -273,31 +276,34 @@ __device__ __forceinline__ void store_row_block(const uint32_t (&o)[TILES][4][4]
 // MFMA column tiles 2jj and 2jj + 1 of a wave tile carry the two accumulators of
 // the same 32 outputs in the same lanes, and the epilogue writes
 // y = acc1 * (alpha_a * alpha1) + acc2 * (alpha_a * alpha2) to N / 2 columns.
+constexpr int kBand = 8;  // tile rows per band of the tile order
+
+// One block's tile: the whole kernel but for the block's index `vblk` among the
+// `vnblk` blocks of its part of the launch (the launch, or one part of a
+// two-part launch).
 template <bool B_TERNARY, int OUT, int S, bool RES = false, bool PAIR = false>
-__global__ void __launch_bounds__((PAIR ? 2 : S) * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__ a_sign,
-                 const float* __restrict__ a_alpha, int64_t a_batch_rows,
-                 const uint8_t* __restrict__ b_mask, const uint8_t* __restrict__ b_sign,
-                 const float* __restrict__ b_alpha, int64_t b_batch_rows, int64_t M, int64_t N,
-                 int64_t row_bytes, int tiles_m, int tiles_n, void* __restrict__ Y, int64_t ldy,
-                 int64_t y_batch_stride, int tile0) {
+__device__ __forceinline__ void gemm_tile(
+    const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__ a_sign,
+    const float* __restrict__ a_alpha, int64_t a_batch_rows, const uint8_t* __restrict__ b_mask,
+    const uint8_t* __restrict__ b_sign, const float* __restrict__ b_alpha, int64_t b_batch_rows,
+    int64_t M, int64_t N, int64_t row_bytes, int tiles_m, int tiles_n, void* __restrict__ Y,
+    int64_t ldy, int64_t y_batch_stride, int tile0, int vblk, int vnblk) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = __lane_id();
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int r = lane & 31;
   const int g = lane >> 5;
 
-  // The launch covers tiles tile0 .. tile0 + gridDim.x - 1 of the tile order
+  // The part covers tiles tile0 .. tile0 + vnblk - 1 of the tile order
   // below.  Blocks are dealt round-robin to the 8 XCDs; give each XCD a
   // contiguous run of that order, whose tiles then share A and B panels in the
-  // XCD's L2.  Order: bands of kBand tile rows, column by column within a band,
+  // XCD's L2 (a part that starts at a multiple of 8 blocks keeps the deal).  Order: bands of kBand tile rows, column by column within a band,
   // so a run of r tiles spans about kBand rows and r / kBand columns (LLaMA-7B
   // gate and up as separate products, 172 tiles per XCD: 1 MB of A and 1.4 MB of
   // B panels, against 0.25 MB and all 5.6 MB of B for row-major runs).
-  constexpr int kBand = 8;
-  const int nblk = (int)gridDim.x;
-  int lin = blockIdx.x;
-  if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int nblk = vnblk;
+  int lin = vblk;
+  if ((nblk & 7) == 0) lin = (vblk & 7) * (nblk >> 3) + (vblk >> 3);
   lin += tile0;
   // PAIR: the order runs over column pairs; wave w takes column 2c + w (a
   // missing last column repeats column tiles_n - 1 and stores nothing)
@@ -770,6 +776,44 @@ gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__
   }
 }
 
+template <bool B_TERNARY, int OUT, int S, bool RES = false, bool PAIR = false>
+__global__ void __launch_bounds__((PAIR ? 2 : S) * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_mfma_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__ a_sign,
+                 const float* __restrict__ a_alpha, int64_t a_batch_rows,
+                 const uint8_t* __restrict__ b_mask, const uint8_t* __restrict__ b_sign,
+                 const float* __restrict__ b_alpha, int64_t b_batch_rows, int64_t M, int64_t N,
+                 int64_t row_bytes, int tiles_m, int tiles_n, void* __restrict__ Y, int64_t ldy,
+                 int64_t y_batch_stride, int tile0) {
+  gemm_tile<B_TERNARY, OUT, S, RES, PAIR>(a_mask, a_sign, a_alpha, a_batch_rows, b_mask, b_sign,
+                                          b_alpha, b_batch_rows, M, N, row_bytes, tiles_m, tiles_n,
+                                          Y, ldy, y_batch_stride, tile0, (int)blockIdx.x,
+                                          (int)gridDim.x);
+}
+
+// Two parts in one launch of two-wave blocks: blocks [0, npair) run paired waves
+// over the first npair column pairs of the pair order (2 npair whole tiles),
+// the rest split K in two over the single-tile order from tile 2 npair on (the
+// host checks that the two orders cover the same first 2 npair tiles).  The
+// second part's blocks start as the first part's retire, under their output
+// stores, with no launch gap between the parts.
+template <bool B_TERNARY, int OUT, bool RES = false>
+__global__ void __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_mfma_two_kernel(const uint8_t* __restrict__ a_mask, const uint8_t* __restrict__ a_sign,
+                     const float* __restrict__ a_alpha, const uint8_t* __restrict__ b_mask,
+                     const uint8_t* __restrict__ b_sign, const float* __restrict__ b_alpha,
+                     int64_t M, int64_t N, int64_t row_bytes, int tiles_m, int tiles_n,
+                     void* __restrict__ Y, int64_t ldy, int npair) {
+  if ((int)blockIdx.x < npair)
+    gemm_tile<B_TERNARY, OUT, 1, RES, true>(a_mask, a_sign, a_alpha, 0, b_mask, b_sign, b_alpha, 0,
+                                            M, N, row_bytes, tiles_m, tiles_n, Y, ldy, 0, 0,
+                                            (int)blockIdx.x, npair);
+  else
+    gemm_tile<B_TERNARY, OUT, 2, RES, false>(a_mask, a_sign, a_alpha, 0, b_mask, b_sign, b_alpha,
+                                             0, M, N, row_bytes, tiles_m, tiles_n, Y, ldy, 0,
+                                             2 * npair, (int)blockIdx.x - npair,
+                                             (int)gridDim.x - npair);
+}
+
 // Split K over S waves when that fills more SIMDs: minimise rounds(S) / S, where a
 // round is one wave on each of the 1024 SIMDs; no more waves than 256-k steps
 // (BERT's 768 x 768 product, 3 steps on 192 tiles, takes S = 2: 384 waves of one
@@ -808,6 +852,53 @@ hipError_t launch_k(const GemmArgs& g, int64_t row_bytes, int64_t tm, int64_t tn
   return hipGetLastError();
 }
 
+// Tile (row, column) of entry `lin` of the tile order (pair order: column pairs),
+// as the kernel computes it.
+void order_tile(int64_t lin, int64_t tm, int64_t tn, bool pair, int w, int64_t& r, int64_t& c) {
+  const int64_t tn_order = pair ? (tn + 1) / 2 : tn;
+  const int64_t band = lin / (kBand * tn_order);
+  const int64_t band_rows = std::min<int64_t>(kBand, tm - band * kBand);
+  const int64_t in_band = lin - band * kBand * tn_order;
+  const int64_t tc = in_band / band_rows;
+  r = band * kBand + (in_band - tc * band_rows);
+  c = pair ? 2 * tc + w : tc;
+}
+
+// Whether the first npair entries of the pair order cover exactly the first
+// 2 npair tiles of the single-tile order (then one two-part launch can run them).
+bool pair_prefix_matches(int64_t tm, int64_t tn, int64_t npair) {
+  if (tn % 2 != 0 || 2 * npair > tm * tn) return false;
+  std::vector<char> seen((size_t)(tm * tn), 0);
+  for (int64_t p = 0; p < npair; ++p)
+    for (int w = 0; w < 2; ++w) {
+      int64_t r, c;
+      order_tile(p, tm, tn, true, w, r, c);
+      seen[(size_t)(r * tn + c)] = 1;
+    }
+  for (int64_t t = 0; t < 2 * npair; ++t) {
+    int64_t r, c;
+    order_tile(t, tm, tn, false, 0, r, c);
+    if (!seen[(size_t)(r * tn + c)]) return false;
+  }
+  return true;
+}
+
+template <bool B_TERNARY, int OUT, bool RES = false>
+hipError_t launch_two(const GemmArgs& g, int64_t row_bytes, int64_t tm, int64_t tn, int64_t npair,
+                      int64_t rest, hipStream_t stream) {
+  size_t lds = (size_t)kRing * Stage<B_TERNARY, true>::kBytes;
+  lds = std::max(lds, (size_t)2 * kRing * Stage<B_TERNARY>::kBytes);
+  lds = std::max(lds, kXchgBytes);
+  auto kfn = gemm_mfma_two_kernel<B_TERNARY, OUT, RES>;
+  hipError_t e =
+      hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kfn, dim3((unsigned)(npair + rest)), dim3(2 * kWave), lds, stream, g.a_mask,
+                     g.a_sign, g.a_alpha, g.b_mask, g.b_sign, g.b_alpha, g.M, g.N, row_bytes,
+                     (int)tm, (int)tn, g.Y, g.ldy, (int)npair);
+  return hipGetLastError();
+}
+
 template <bool B_TERNARY, int OUT, bool RES = false>
 hipError_t launch_s(const GemmArgs& g, int S, int64_t row_bytes, int64_t tm, int64_t tn,
                     int64_t tile0, int64_t tiles, hipStream_t stream) {
@@ -842,6 +933,11 @@ hipError_t launch_plan(const GemmArgs& g, int64_t row_bytes, int64_t tm, int64_t
                                          tn, 0, tiles, stream);
   const int64_t rem = tiles % simds;
   if (g.batch == 1 && rem > 0 && rem <= simds / 2 && steps >= 4) {
+    // One launch for both parts where the pair order allows it (even column
+    // count, whole column pairs in the first part, parts on 8-block boundaries).
+    const int64_t npair = (tiles - rem) / 2;
+    if (npair % 8 == 0 && pair_prefix_matches(tm, tn, npair))
+      return launch_two<B_TERNARY, OUT, RES>(g, row_bytes, tm, tn, npair, rem, stream);
     const hipError_t e =
         launch_s<B_TERNARY, OUT, RES>(g, 1, row_bytes, tm, tn, 0, tiles - rem, stream);
     if (e != hipSuccess) return e;

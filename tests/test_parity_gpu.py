@@ -217,8 +217,9 @@ def test_gemm_ldy_complete_tiles(bw, oracle, out_dtype):
 
 # Grids of more 128 x 128 output tiles than the chip's 1024 SIMDs: whole rounds
 # run one tile per wave over all of K, the last partial round (at most 512
-# tiles) splits each tile's K range over two waves, both kinds of blocks in one
-# launch.  Outputs start as a sentinel, every output is checked against the
+# tiles) splits each tile's K range over two waves - in one launch of two-wave
+# blocks (paired waves for the whole rounds) where the column count is even and
+# the whole rounds end on whole column pairs, else as a second launch.  Outputs start as a sentinel, every output is checked against the
 # properties |acc| <= nnz and acc = nnz (mod 2), and all rows against the oracle
 # on two columns of every 128-column tile.
 # Grids that stay one unsplit launch (a partial round above 512 tiles, or fewer
@@ -227,7 +228,11 @@ def test_gemm_ldy_complete_tiles(bw, oracle, out_dtype):
 GRID_SHAPES = [(2048, 8300, 1000),   # 16 x 65 tiles = 1024 + 16; ragged N, ragged K
                (1900, 8960, 1536),   # 15 x 70 tiles = 1024 + 26; ragged M
                (1000, 24654, 300),   # 8 x 193 tiles = 1024 + 520: pairs, odd columns
-               (1100, 16500, 500)]   # 9 x 129 tiles, 2 steps of K: pairs, odd columns
+               (1100, 16500, 500),   # 9 x 129 tiles, 2 steps of K: pairs, odd columns
+               (2048, 12288, 1000),  # 16 x 96 = 1024 + 512 in one launch; ragged K
+               (2000, 12288, 2000),  # the same grid, ragged M, 8 steps of K
+               (1536, 16384, 800),   # 12 x 128 in one launch: bands of 8 and 4 rows
+               (1024, 20480, 1100)]  # 8 x 160 = 1024 + 256 in one launch
 
 
 def _grid_columns(N, seed):
@@ -403,6 +408,39 @@ def test_batched_grid_pairs_scaled(bw, oracle, out_dtype):
             assert (got[h] == oracle.to_bf16(ref)).all(), f"head {h}"
         else:
             assert (got[h].view(np.uint32) == ref.view(np.uint32)).all(), f"head {h}"
+
+@pytest.mark.parametrize("out_dtype", ["i32", "f32"])
+def test_batched_two_part_ternary(bw, oracle, out_dtype):
+    """One batch of a ternary x ternary product on a 16 x 96 tile grid (2048 x
+    12288, K = 1000): the one-launch two-part grid with ternary B planes (paired
+    waves on 1024 tiles, K split in two on the last 512); sentinel-filled output,
+    all rows on two columns of every tile, every score within |acc| <= nnz."""
+    import torch
+    M, N, K = 2048, 12288, 1000
+    rng = np.random.Generator(np.random.PCG64(M + N + K))
+    q = inputs.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    k = inputs.f32_to_bf16_bits(rng.standard_normal((N, K), dtype=np.float32) * 1.3)
+    qa = bw.bwta_ternarize_pack(to_dev(q))
+    ka = bw.bwta_ternarize_pack(to_dev(k))
+    tdt = torch.int32 if out_dtype == "i32" else torch.float32
+    fill = 0x7FFFFFFF if out_dtype == "i32" else float("nan")
+    out = torch.full((1, M, N), fill, dtype=tdt, device="cuda")
+    got = to_host(bw.bwta_batched_gemm(1, qa, M, ka, N, M, N, out_dtype=out_dtype, algo="mfma",
+                                       out=out))[0]
+    tq, aq, nq = oracle.ternarize(q)
+    tk, ak, _ = oracle.ternarize(k)
+    C = _grid_columns(N, 5)
+    ref = oracle.matmul_i32(tq, tk[C], threads=8)
+    if out_dtype == "i32":
+        acc = got.astype(np.int64)
+        nz = nq.astype(np.int64)[:, None]
+        assert (np.abs(acc) <= nz).all(), "a score breaks |acc| <= nnz"  # (no parity rule: B is ternary)
+        assert (acc[:, C] == ref).all(), f"{(acc[:, C] != ref).sum()} scores differ"
+    else:
+        assert not np.isnan(got).any(), "outputs left unwritten"
+        want = oracle.scale(ref, aq, ak[C])
+        assert (got[:, C].view(np.uint32) == want.view(np.uint32)).all()
+
 
 def test_pack_weights_columns_all_heads(bw, oracle):
     """V laid out [L, H*D]: one call packs V^T of every head (row h*D + d)."""

@@ -106,12 +106,13 @@ def test_gemm_residual_ldy(bw, oracle, K):
     assert (got[:, N:] == 7.0).all()
 
 
-def test_gemm_residual_grid_rounds(bw, oracle):
+@pytest.mark.parametrize("M,N,K", [(2048, 4160, 1000), (2048, 6144, 1000)])
+def test_gemm_residual_grid_rounds(bw, oracle, M, N, K):
     """16 x 65 plane tiles (4160 outputs, 8320 plane rows): 1024 tiles one per wave,
-    the last 16 split over K; NaN-filled output, all rows on two columns of every
-    64-output tile."""
+    the last 16 split over K in a second launch; 16 x 96 plane tiles (6144 outputs):
+    512 blocks of paired waves and 512 blocks that split K in one launch.
+    NaN-filled output, all rows on two columns of every 64-output tile."""
     import torch
-    M, N, K = 2048, 4160, 1000
     x, w = inputs.random_linear(4242, M, K, N)
     a = bw.bwta_ternarize_pack(to_dev(x))
     wp = bw.bwta_pack_weights_residual(to_dev(w))
