@@ -667,6 +667,8 @@ def main():
                     help="only the measured ceilings (HBM read streams, MFMA loops)")
     ap.add_argument("--gemv", action="store_true",
                     help="only the decode section (GEMV shapes and the decode linear end to end)")
+    ap.add_argument("--bert", action="store_true",
+                    help="only the BERT-base encoder linears (ternarize + product each)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -693,6 +695,9 @@ def main():
         return
     if args.gemv:
         print(json.dumps({"gemv": bench_gemv(bw)}), flush=True)
+        return
+    if args.bert:
+        print(json.dumps({"bert": bench_bert(bw)}), flush=True)
         return
 
     from binary_ternary_matmul_amd import inputs
