@@ -224,13 +224,16 @@ def bwta_ternarize_pack(X: torch.Tensor) -> TernaryPlanes:
 
 
 _WORKSPACE = {}  # device index -> zero-filled uint8 tensor (the "auto" workspaces)
+_RETIRED = []    # workspaces replaced by larger ones: captured graphs may still use them
 
 
 def workspace(device, nbytes: int) -> torch.Tensor:
     """A zero-filled workspace of at least nbytes on `device`, shared by every
     call that asks for "auto" (the library leaves its counters zero after each
     call, so one buffer serves all calls on a stream).  Grown outside graph
-    capture only: warm a captured call up once first."""
+    capture only: warm a captured call up once first.  A buffer that is
+    replaced by a larger one stays allocated, so graphs captured on it remain
+    valid (each keeps its own counters zero between replays)."""
     dev = torch.device(device)
     idx = dev.index if dev.index is not None else torch.cuda.current_device()
     ws = _WORKSPACE.get(idx)
@@ -238,6 +241,8 @@ def workspace(device, nbytes: int) -> torch.Tensor:
         if torch.cuda.is_current_stream_capturing():
             raise RuntimeError("the shared workspace must grow, which cannot happen during "
                                "graph capture: run the call once before capturing it")
+        if ws is not None:
+            _RETIRED.append(ws)
         ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _WORKSPACE[idx] = ws
     return ws
