@@ -19,6 +19,9 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(1, 1000, 1024), (2, 513, 8192), (4, 300, 28672), (16, 300, 28672), (3, 77, 200),
           (1, 40, 65536), (5, 100, 100), (7, 257, 1000), (4, 33, 64), (1, 17, 1),
           (16, 1000, 28736), (9, 600, 36928),
+          # the longest rows at M >= 2: the producing blocks read each row twice
+          # (more than 8 runs of 8 values per thread), with the cross-block split
+          (16, 300, 65536), (3, 513, 65536),
           # one row: the single-row kernel's launch shapes (4-, 8- and 16-wave blocks,
           # one, two and four 1 KiB chunks per weight row, ragged N and K) and plane
           # rows of an odd number of 8-byte words (12344, 4104: the general kernel)
@@ -89,7 +92,8 @@ def test_gemv_fused_zero_rows(bw, oracle):
 # every block (the kernel still ends normally; the rows are written several times
 # with the same values).
 @pytest.mark.parametrize("M,N,K", [(2, 513, 8192), (16, 300, 28672), (5, 100, 100),
-                                   (9, 600, 36928), (1, 8200, 12344), (3, 77, 200)])
+                                   (9, 600, 36928), (1, 8200, 12344), (3, 77, 200),
+                                   (4, 64, 65536)])
 def test_gemv_fused_every_block_ternarizes(bw, oracle, M, N, K):
     x = _x(M * 7 + N, M, K, True)
     w = _w(N * 3 + K, N, K)
