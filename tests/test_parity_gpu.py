@@ -232,7 +232,8 @@ GRID_SHAPES = [(2048, 8300, 1000),   # 16 x 65 tiles = 1024 + 16; ragged N, ragg
                (2048, 12288, 1000),  # 16 x 96 = 1024 + 512 in one launch; ragged K
                (2000, 12288, 2000),  # the same grid, ragged M, 8 steps of K
                (1536, 16384, 800),   # 12 x 128 in one launch: bands of 8 and 4 rows
-               (1024, 20480, 1100)]  # 8 x 160 = 1024 + 256 in one launch
+               (1024, 20480, 1100),  # 8 x 160 = 1024 + 256 in one launch
+               (2048, 12200, 1000)]  # 16 x 96 in one launch, ragged last column
 
 
 def _grid_columns(N, seed):
