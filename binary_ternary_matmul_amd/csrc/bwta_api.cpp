@@ -93,17 +93,28 @@ bwta_status check_product(const uint8_t* a_mask, const uint8_t* a_sign, const fl
   return BWTA_OK;
 }
 
+// AUTO on a decode product (binary B): one activation row, or two whose plane
+// rows are whole 16-byte units, cost the popcount GEMV one merge and one
+// population count per weight word and row, less than building FP4 operands
+// (LLaMA2-70B gate/up and down at M = 2: 8.25 and 8.37 us against 8.43 and
+// 8.97 us); from three rows on the FP4 GEMV, whose cost does not grow with M,
+// is faster (M = 3: 17.8 against 8.4 us).
+bool auto_popcount_decode(int64_t M, int64_t K) {
+  return M <= 1 || (M == 2 && ((K + 63) / 64 * 8) % 16 == 0);
+}
+
 // Workspace bytes of one product call: the decode kernel's cross-block K split
-// is the only user.  gemv: the FP4 decode kernel (AUTO from two rows on, MFMA,
-// MFMA_I8); gemm: AUTO sends M <= 16 to the same decode kernels.
+// is the only user.  gemv: the FP4 decode kernel (AUTO where the popcount GEMV
+// does not take the rows, MFMA, MFMA_I8); gemm: AUTO sends M <= 16 to the same
+// decode kernels.
 size_t product_workspace(int64_t M, int64_t N, int64_t K, bwta_algo algo, bool gemv) {
   if (M <= 0 || N <= 0 || K <= 0 || K > BWTA_MAX_K || M > 16) return 0;
   bool fp4_decode;
   if (gemv)
     fp4_decode = algo == BWTA_ALGO_MFMA || algo == BWTA_ALGO_MFMA_I8 ||
-                 (algo == BWTA_ALGO_AUTO && M >= 2);
+                 (algo == BWTA_ALGO_AUTO && !auto_popcount_decode(M, K));
   else
-    fp4_decode = algo == BWTA_ALGO_AUTO && M >= 2;
+    fp4_decode = algo == BWTA_ALGO_AUTO && !auto_popcount_decode(M, K);
   return fp4_decode ? bwta::gemv_mfma_workspace_bytes(M, N, K) : 0;
 }
 
@@ -205,12 +216,9 @@ static bwta_status run_product(const bwta::GemmArgs& g, bwta_algo algo, bool gem
   // A single (unbatched) product of at most 16 activation rows is a decode
   // product: with AUTO, bwta_gemm runs it on the decode kernels as well.
   if (!gemv && algo == BWTA_ALGO_AUTO && g.batch == 1 && !g.b_mask && g.M <= 16) gemv = true;
-  if (algo == BWTA_ALGO_AUTO) {
-    // Decode: a single activation row costs the popcount GEMV one merge and one
-    // population count per weight word, less than building FP4 operands; from
-    // two rows on the FP4 GEMV, whose cost does not grow with M, is faster.
-    algo = (gemv && g.M <= 1 && !g.b_mask) ? BWTA_ALGO_POPCOUNT : BWTA_ALGO_MFMA;
-  }
+  if (algo == BWTA_ALGO_AUTO)
+    algo = (gemv && !g.b_mask && auto_popcount_decode(g.M, g.K)) ? BWTA_ALGO_POPCOUNT
+                                                                 : BWTA_ALGO_MFMA;
   hipError_t e;
   if (gemv && !g.b_mask && (algo == BWTA_ALGO_MFMA || algo == BWTA_ALGO_MFMA_I8)) {
     // Decode: the skinny FP4 kernel streams the weights once for any M <= 16.

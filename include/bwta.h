@@ -80,8 +80,9 @@ typedef enum {
 typedef enum { BWTA_F32 = 0, BWTA_BF16 = 1, BWTA_I32 = 2 } bwta_dtype;
 
 /* Kernel family for the products.  All give the same exact sums.
- *   AUTO      picks the fastest: MFMA, except the popcount GEMV for bwta_gemv
- *             with M = 1.
+ *   AUTO      picks the fastest: MFMA, except the popcount GEMV for decode
+ *             products of one row, or of two rows whose plane rows are whole
+ *             16-byte units.
  *   MFMA      expands the bit planes to FP4 (e2m1) {-1, 0, +1} and multiplies
  *             on the FP4 matrix cores with unit block scales and fp32
  *             accumulation; every partial sum is an integer below 2^24, so the
